@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark one H3-Omni-Transformer block forward on one MI355X.
+
+Workload (default): the 15 s 16:9 768p packed sequence -- 512 text tokens,
+600 audio tokens and a 91 x 24 x 42 video grid (92840 tokens) -- through a
+full-width bf16 block (hidden 5376, 56 heads x 128, FFN 14336) with seeded
+synthetic activations and random-init weights.  A step is one block forward:
+the eleven libh3blk calls on one stream, inputs already resident in HBM.
+
+Prints one JSON line: block tokens/s (`value`), attention TFLOP/s and % of
+the 2.5 PFLOP/s dense bf16 MFMA peak, per-kernel times, the roofline of the
+dominant kernel (attention) and the fp64 oracle timed on host cores on a
+bounded token sample (`cpu_baseline`).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "H3 block fwd tokens/s + attention bf16 TFLOPS (% peak), 768p 15s seq"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "video_audio_diffusion_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def step_bytes(cfg):
+    """Algorithmic HBM bytes per launch of the streaming passes."""
+    N, D, I, F = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn
+    e = 2 if cfg.dtype == "bf16" else 4
+    return {"adaln_attn": 2 * N * D * e, "adaln_ffn": 2 * N * D * e,
+            "qknorm_rope": 4 * N * I * e, "swiglu": 3 * N * F * e,
+            "gate_attn": 3 * N * D * e, "gate_ffn": 3 * N * D * e}
+
+
+def step_flops(cfg):
+    N, D, H, d, I, F = cfg.n_tok, cfg.dim, cfg.heads, cfg.head_dim, cfg.inner, cfg.ffn
+    return {"gemm_qkv": 2 * N * D * 3 * I, "attention": 4 * N * N * H * d, "gemm_o": 2 * N * I * D,
+            "gemm_gu": 2 * N * D * 2 * F, "gemm_d": 2 * N * F * D}
+
+
+def cpu_baseline(cfg, host, target_s):
+    """The fp64 oracle, as it stands, on a token sample of the same workload.
+
+    Every step but attention is row-wise, and attention's cost per query row
+    is one sweep over all keys, so whole-block time is the sum of per-token
+    costs: the oracle runs all eleven steps for S sampled tokens (their q, k,
+    v included) against a full-length K/V of the same shape (other tokens'
+    work, filled untimed), and tokens/s = S / time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from video_audio_diffusion_amd import inputs
+
+    N, H, d, I, F = cfg.n_tok, cfg.heads, cfg.head_dim, cfg.inner, cfg.ffn
+    seg, eps = cfg.segments, cfg.eps
+    t = {k: inputs.widen(host[k], cfg.dtype) for k in ("w_qkv", "w_o", "w_gu", "w_d")}
+    mod = host["mod"].astype(np.float64)
+    gq, gk = host["gamma_q"].astype(np.float64), host["gamma_k"].astype(np.float64)
+    blk0 = inputs.widen(inputs.draw_rows(cfg, (1024, 2 * I), 4242), cfg.dtype)
+    reps = (N + 1023) // 1024
+    K_all = np.tile(blk0[:, :I], (reps, 1))[:N]
+    V_all = np.tile(blk0[:, I:], (reps, 1))[:N]
+    _, pos = oracle.token_table(seg, N)
+    g = np.random.Generator(np.random.PCG64(99))
+    perm = g.permutation(N)
+
+    def run(rows):
+        rows = np.sort(rows)
+        x = inputs.widen(host["x"][rows], cfg.dtype)
+        a = oracle.adaln_modulate(x, mod, 0, seg, eps, rows=rows)
+        qkv = oracle.linear(a, t["w_qkv"])
+        q = oracle.rope3d(oracle.qk_rmsnorm(qkv[:, :I], H, d, gq, eps), pos[rows], H, d, cfg.rope_split,
+                          cfg.rope_base)
+        oracle.rope3d(oracle.qk_rmsnorm(qkv[:, I:2 * I], H, d, gk, eps), pos[rows], H, d, cfg.rope_split,
+                      cfg.rope_base)
+        o = oracle.attention(q, K_all, V_all, H, d, cfg.scale, rows=rows)
+        x1 = oracle.gate_residual(x, oracle.linear(o, t["w_o"]), mod, 0, seg, rows=rows)
+        a2 = oracle.adaln_modulate(x1, mod, 1, seg, eps, rows=rows)
+        h = oracle.swiglu(oracle.linear(a2, t["w_gu"]), F)
+        return oracle.gate_residual(x1, oracle.linear(h, t["w_d"]), mod, 1, seg, rows=rows)
+
+    t0 = time.perf_counter()
+    run(perm[:32])
+    per_row = (time.perf_counter() - t0) / 32
+    S = int(min(max(target_s / per_row, 32), 4096))
+    log(f"cpu baseline: {per_row * 1e3:.1f} ms/token in calibration, timing {S} tokens")
+    t0 = time.perf_counter()
+    run(perm[32:32 + S])
+    el = time.perf_counter() - t0
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    return {"value": S / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{S} random tokens of the {N}-token sequence through all eleven fp64 steps "
+                      f"(their own q/k/v included) against a full {N}-key K/V; {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index (1-4)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 skips it")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the block on one GPU only; there is no multi-GPU path "
+              "(how it would shard is a design note), so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from video_audio_diffusion_amd import blk, inputs
+    from video_audio_diffusion_amd.block import BlockWeights, H3Block, device_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    blk.load()
+    cfg = inputs.CONFIGS[args.config]
+    log(f"workload {cfg.name}: {cfg.n_tok} tokens; drawing inputs")
+    host = inputs.make_inputs(cfg)
+    dev = device_inputs(cfg, host)
+    log("inputs resident on device")
+    block = H3Block(cfg, BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
+                                      dev["gamma_q"], dev["gamma_k"]))
+    x = dev["x"]
+    for i in range(args.warmup):
+        block.forward(x)
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        block.forward(x, events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][11])
+    ms_step = total_ms / K
+    log(f"timed {K} steps: {ms_step:.2f} ms/step (host wall {wall * 1e3 / K:.2f} ms/step)")
+
+    per = {name: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+           for j, name in enumerate(H3Block.STEPS)}
+    flops, byts = step_flops(cfg), step_bytes(cfg)
+    peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    kernels = {}
+    for name, ms in per.items():
+        k = {"ms": round(ms, 4)}
+        if name in flops:
+            tf = flops[name] / (ms * 1e-3) / 1e12
+            k.update(tflops=round(tf, 1), frac_peak=round(tf / peak_mm, 4))
+        else:
+            gbs = byts[name] / (ms * 1e-3) / 1e9
+            k.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = k
+    attn_tf = flops["attention"] / (per["attention"] * 1e-3) / 1e12
+    tokens_s = cfg.n_tok * K / (total_ms * 1e-3)
+
+    result = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name} block forward", "tokens": cfg.n_tok,
+                   "segments": [f"{s.kind} {s.T}x{s.H}x{s.W}" for s in cfg.segments],
+                   "hidden": cfg.dim, "heads": cfg.heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
+                   "rope_split": list(cfg.rope_split), "global_batch": 1, "seq_len": cfg.n_tok,
+                   "parallelism": "none (1 GPU)"},
+        "attention_tflops": round(attn_tf, 1), "attention_pct_peak": round(100 * attn_tf / peak_mm, 2),
+        "kernels": kernels,
+        "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(attn_tf, 1), "peak": peak_mm,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / peak_mm, 4),
+                     "traffic": measured_traffic("attention"),
+                     "algorithmic_per_launch": f"{flops['attention']:.4e} flop (4*N^2*heads*head_dim)"},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        log("timing the fp64 oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(cfg, host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

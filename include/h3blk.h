@@ -1,0 +1,167 @@
+/*
+ * libh3blk -- one MiniMax H3 Omni-Transformer block forward on an AMD
+ * Instinct MI355X (gfx950), as six device calls.
+ *
+ * Sources cited below by short name:
+ *   [notes]   "05 · MiniMax-H3: native audio-video joint generation"
+ *             (note.shouss.top/research/video_generation/minimax_h3/)
+ *   [reading] "MiniMax-H3 paper reading" (gojay.top/paper-reading/minimax-h3.html)
+ *
+ * A block forward is, per [notes] section 3:
+ *   a   = h3_adaln_modulate(x, ATTN)          modulated norm
+ *   qkv = h3_gemm_bf16(a, W_qkv)              5376 -> 3 x 7168
+ *   h3_qknorm_rope3d(q, k)                    per-head RMSNorm, then 3-D RoPE
+ *   o   = h3_attention_fwd(q, k, v)           full bidirectional attention
+ *   y   = h3_gemm_bf16(o, W_o)                7168 -> 5376
+ *   x1  = h3_gate_residual(x, y, ATTN)        x + gate * y
+ *   a2  = h3_adaln_modulate(x1, FFN)
+ *   gu  = h3_gemm_bf16(a2, W_gu)              5376 -> 2 x 14336  [gate | up]
+ *   h   = h3_swiglu(gu)                       SiLU(gate) * up
+ *   f   = h3_gemm_bf16(h, W_d)                14336 -> 5376
+ *   out = h3_gate_residual(x1, f, FFN)
+ *
+ * Conventions shared by every call:
+ *   - Tensors are row-major with tokens as rows.  Every pointer argument is
+ *     a device pointer unless marked "host".  The caller owns all memory;
+ *     the library allocates nothing and keeps no state, so calls may be
+ *     made from several host threads on different streams.
+ *   - `dt` selects the storage type of activations and weights: H3_BF16
+ *     (bf16 storage, fp32 accumulation and epilogue math, round to nearest
+ *     even on every store) or H3_F32 (fp32 everywhere).  The modulation
+ *     table, gains and lse are always fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work and returns; nothing synchronises.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on any error code nothing runs and no output is touched.  Device
+ *     faults surface at the caller's next synchronisation.
+ *   - Pointers must be 16-byte aligned; row strides must keep every row
+ *     16-byte aligned (a multiple of 8 bf16 or 4 fp32 elements).
+ *   - n_tok == 0 (or M == 0) is valid and enqueues nothing.
+ */
+#ifndef H3BLK_H
+#define H3BLK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    H3_OK = 0,
+    H3_ERR_ARG = 1,       /* null pointer, negative size, bad enum value      */
+    H3_ERR_SEGMENTS = 2,  /* intervals unsorted, overlapping, gapped, not covering
+                             [0, n_tok), len != T*H*W, mod_set out of range   */
+    H3_ERR_DTYPE = 3,     /* unknown dtype                                    */
+    H3_ERR_ALIGN = 4,     /* pointer or row stride breaks 16-byte alignment   */
+    H3_ERR_SHAPE = 5,     /* a size the kernels do not support                */
+    H3_ERR_HIP = 6        /* the HIP runtime refused a launch                 */
+} h3_status;
+
+typedef enum { H3_BF16 = 0, H3_F32 = 1 } h3_dtype;
+
+/* Which half of a modality's six modulation vectors a call uses:
+ * ATTN takes chunks (shift1, scale1, gate1) = 0,1,2; FFN takes 3,4,5. */
+typedef enum { H3_BRANCH_ATTN = 0, H3_BRANCH_FFN = 1 } h3_branch;
+
+/* One interval of the packed multimodal sequence.  [notes] 2.2: the packed
+ * sequence keeps an index range for each interval (text, visual condition,
+ * audio, target video).  Tokens of an interval are a (T, H, W) grid
+ * flattened with t slowest and w fastest ([reading] 7.3); text and audio are
+ * T = len, H = W = 1, so they sit on the time axis with h = w = 0
+ * ([reading] 7.4).  Token l of the interval has 3-D position
+ *   (t0 + l / (H*W), h0 + (l / W) % H, w0 + l % W).
+ * mod_set is the row of the modulation table the interval uses
+ * (by convention 0 text, 1 visual, 2 audio). */
+typedef struct {
+    int64_t start;   /* first token                                   */
+    int64_t len;     /* number of tokens, must equal T*H*W            */
+    int32_t mod_set; /* modulation row, 0 <= mod_set < n_sets         */
+    int32_t T, H, W; /* grid, each >= 1                               */
+    int32_t t0, h0, w0; /* position offsets, >= 0                     */
+} h3_segment;
+
+#define H3_MAX_SEGMENTS 64
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* h3_status_str(h3_status s);
+
+/* Modulated RMSNorm of [notes] section 3, with the per-interval modality
+ * selection of [notes] 3.1:
+ *   y[i,:] = x[i,:] / sqrt(mean(x[i,:]^2) + eps) * (1 + scale[s(i)]) + shift[s(i)]
+ * where s(i) is the mod_set of the interval holding token i, and shift/scale
+ * are chunks (3*br, 3*br+1) of mod.
+ *   x, y : [n_tok][dim] in dt, contiguous (may not alias)
+ *   mod  : fp32 [n_sets][6][dim], contiguous
+ *   segs : host array of n_segs intervals (1..64) covering [0, n_tok)
+ * dim must be a multiple of 8 and at most 8192 (bf16) / 4096 (fp32). */
+h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim,
+                            const float* mod, int32_t n_sets, h3_branch br,
+                            const h3_segment* segs, int32_t n_segs, float eps,
+                            h3_dtype dt, void* stream);
+
+/* C = A . W^T: the bias-free projections of the block (QKV, output, FFN
+ * gate/up and down; [notes] 3.2 table).
+ *   A : [M][K] with row stride lda (elements)
+ *   W : [N][K] with row stride ldw (weights stored out-features major)
+ *   C : [M][N] with row stride ldc; must not overlap A or W
+ * bf16: K a multiple of 64; fp32: K a multiple of 32; N a multiple of 8.
+ * Accumulation is fp32 in MFMA; C is rounded once. */
+h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw,
+                       void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                       h3_dtype dt, void* stream);
+
+/* Per-head RMSNorm on Q and K ([notes] 3.2: applied per head, before the
+ * positional encoding), then 3-D MM-RoPE ([reading] 5 and 7.4), in place:
+ *   u <- gamma * u / sqrt(mean(u^2) + eps)      over each head's head_dim values
+ *   then inside each head the dims are cut into [t: d_t | h: d_h | w: d_w];
+ *   adjacent pairs (2j, 2j+1) of the chunk of axis a are rotated by the angle
+ *   p_a * rope_base^(-2j/d_a), p_a the token's position on axis a:
+ *     (u0, u1) <- (u0 cos - u1 sin, u0 sin + u1 cos).
+ *   q, k    : [n_tok][heads*head_dim] views with row stride ld (elements),
+ *             e.g. the q and k column blocks of the QKV output
+ *   gamma_q, gamma_k : fp32 [head_dim], or NULL for a gain of 1
+ *   segs    : host intervals giving every token's (t, h, w)
+ * head_dim in {64, 128}; d_t, d_h, d_w even, >= 0, summing to head_dim. */
+h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok,
+                           int32_t heads, int32_t head_dim,
+                           const float* gamma_q, const float* gamma_k, float eps,
+                           int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
+                           const h3_segment* segs, int32_t n_segs,
+                           h3_dtype dt, void* stream);
+
+/* Full bidirectional softmax attention per head ([notes] section 5: one
+ * non-causal self-attention over all valid tokens, no mask):
+ *   o[i, h] = sum_j softmax_j(scale * q[i,h] . k[j,h]) v[j,h]
+ *   q, k, v : [n_tok][heads*head_dim] views sharing row stride ld_qkv
+ *   o       : [n_tok][heads*head_dim] with row stride ld_o (must not alias q/k/v)
+ *   lse     : optional fp32 [heads][n_tok], receives
+ *             log(sum_j exp(scale * q[i,h] . k[j,h])) (natural log); NULL to skip
+ * head_dim in {64, 128}; n_tok < 2^31. */
+h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv,
+                           void* o, int64_t ld_o, int64_t n_tok, int32_t heads,
+                           int32_t head_dim, float scale, float* lse,
+                           h3_dtype dt, void* stream);
+
+/* SwiGLU of the gated FFN ([notes] 3.2): h = SiLU(g) * u, SiLU(z) = z / (1 + e^-z).
+ *   gu : [n_tok][2F] holding [gate | up]
+ *   h  : [n_tok][F]
+ * F a multiple of 8. */
+h3_status h3_swiglu(const void* gu, void* h, int64_t n_tok, int32_t F,
+                    h3_dtype dt, void* stream);
+
+/* Modality-gated residual ([notes] section 3: "modality gate + residual"):
+ *   out[i,:] = x[i,:] + gate[s(i)] * y[i,:],  gate = chunk 3*br+2 of mod.
+ *   x, y, out : [n_tok][dim] contiguous; out may equal x (in place), must not
+ *               partially overlap x or y.
+ * dim a multiple of 8. */
+h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_tok,
+                           int32_t dim, const float* mod, int32_t n_sets, h3_branch br,
+                           const h3_segment* segs, int32_t n_segs,
+                           h3_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3BLK_H */

@@ -1,0 +1,187 @@
+"""C-ABI checks that need no GPU: the library loads, exports every call the
+header declares, and rejects every kind of bad argument before touching the
+device.  Pointers here are fake (never dereferenced): validation fails first,
+or, for valid arguments on a machine with no GPU, the launch fails with
+H3_ERR_HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_audio_diffusion_amd import blk, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x7f0000000000            # fake, 16-byte aligned device addresses
+CFG1 = inputs.CONFIGS[1]
+CFG2 = inputs.CONFIGS[2]
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return blk.load()
+
+
+def test_exports_every_header_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "h3blk.h")).read()
+    declared = set(re.findall(r"^\s*(?:h3_status|const char\*)\s+(h3_\w+)\(", hdr, re.M))
+    assert declared == set(blk.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert isinstance(blk.status_str(s), str) and blk.status_str(s)
+    assert blk.status_str(99) == "unknown status"
+
+
+def test_segment_struct_layout():
+    assert ctypes.sizeof(blk.H3Segment) == 48
+    assert blk.H3Segment.T.offset == 20 and blk.H3Segment.w0.offset == 40
+
+
+def _adaln(segs=None, n_segs=None, **kw):
+    a = dict(x=P, y=P + (1 << 30), n_tok=CFG1.n_tok, dim=CFG1.dim, mod=P + (2 << 30), n_sets=3, br=0,
+             eps=1e-6, dt=blk.H3_F32)
+    a.update(kw)
+    segs = blk.segments(CFG1.segments) if segs is None else segs
+    n_segs = len(CFG1.segments) if n_segs is None else n_segs
+    return blk.load().h3_adaln_modulate(a["x"], a["y"], a["n_tok"], a["dim"], a["mod"], a["n_sets"], a["br"],
+                                        segs, n_segs, a["eps"], a["dt"], 0)
+
+
+def test_adaln_validation(lib):
+    assert _adaln(dt=5) == blk.H3_ERR_DTYPE
+    assert _adaln(x=0) == blk.H3_ERR_ARG
+    assert _adaln(mod=0) == blk.H3_ERR_ARG
+    assert _adaln(br=2) == blk.H3_ERR_ARG
+    assert _adaln(eps=-1.0) == blk.H3_ERR_ARG
+    assert _adaln(eps=float("nan")) == blk.H3_ERR_ARG
+    assert _adaln(x=P + 4) == blk.H3_ERR_ALIGN
+    assert _adaln(dim=196) == blk.H3_ERR_SHAPE
+    assert _adaln(dim=8192, dt=blk.H3_F32) == blk.H3_ERR_SHAPE     # fp32 rows hold at most 4096
+    assert _adaln(y=P + 64) == blk.H3_ERR_ARG                     # y overlaps x
+    assert _adaln(n_tok=-1) == blk.H3_ERR_ARG
+
+
+def _segs(*rows):
+    arr = (blk.H3Segment * len(rows))()
+    for i, r in enumerate(rows):
+        arr[i] = blk.H3Segment(*r)
+    return arr
+
+
+def test_interval_table_validation(lib):
+    good = [(0, 16, 0, 16, 1, 1, 0, 0, 0), (16, 8, 2, 8, 1, 1, 0, 0, 0), (24, 48, 1, 2, 4, 6, 0, 0, 0)]
+    bad = {
+        "gap": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (17, 8, 2, 8, 1, 1, 0, 0, 0), (25, 47, 1, 47, 1, 1, 0, 0, 0)],
+        "overlap": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (15, 8, 2, 8, 1, 1, 0, 0, 0), (23, 49, 1, 49, 1, 1, 0, 0, 0)],
+        "unsorted": [(16, 8, 2, 8, 1, 1, 0, 0, 0), (0, 16, 0, 16, 1, 1, 0, 0, 0), (24, 48, 1, 2, 4, 6, 0, 0, 0)],
+        "len!=THW": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (16, 8, 2, 8, 1, 1, 0, 0, 0), (24, 48, 1, 2, 4, 5, 0, 0, 0)],
+        "short": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (16, 8, 2, 8, 1, 1, 0, 0, 0)],
+        "long": good + [(72, 1, 0, 1, 1, 1, 0, 0, 0)],
+        "mod_set": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (16, 8, 3, 8, 1, 1, 0, 0, 0), (24, 48, 1, 2, 4, 6, 0, 0, 0)],
+        "neg_offset": [(0, 16, 0, 16, 1, 1, -1, 0, 0), (16, 8, 2, 8, 1, 1, 0, 0, 0), (24, 48, 1, 2, 4, 6, 0, 0, 0)],
+        "zero_grid": [(0, 16, 0, 16, 1, 1, 0, 0, 0), (16, 0, 2, 0, 1, 1, 0, 0, 0), (16, 56, 1, 56, 1, 1, 0, 0, 0)],
+    }
+    for name, rows in bad.items():
+        assert _adaln(segs=_segs(*rows), n_segs=len(rows)) == blk.H3_ERR_SEGMENTS, name
+    many = [(i, 1, 0, 1, 1, 1, 0, 0, 0) for i in range(65)]
+    assert _adaln(segs=_segs(*many), n_segs=65, n_tok=65) == blk.H3_ERR_SEGMENTS
+    assert _adaln(segs=None, n_segs=0) == blk.H3_ERR_SEGMENTS
+    assert blk.load().h3_adaln_modulate(P, P + (1 << 30), 72, 192, P, 3, 0, None, 3, 1e-6, 1, 0) == blk.H3_ERR_ARG
+
+
+def test_empty_sequence_is_a_no_op(lib):
+    # nothing is launched for zero tokens, so this succeeds even with no GPU
+    assert _adaln(n_tok=0, segs=None, n_segs=0) == blk.H3_OK
+    L = blk.load()
+    assert L.h3_gemm_bf16(P, 64, P + (1 << 30), 64, P + (2 << 30), 64, 0, 64, 64, 0, 0) == blk.H3_OK
+    assert L.h3_swiglu(P, P + (1 << 30), 0, 64, 0, 0) == blk.H3_OK
+    assert L.h3_attention_fwd(P, P + 256, P + 512, 384, P + (1 << 30), 128, 0, 1, 128, 0.1, None, 0, 0) == blk.H3_OK
+    assert L.h3_qknorm_rope3d(P, P + 256, 384, 0, 1, 128, None, None, 1e-6, 64, 32, 32, 1e4, None, 0, 0, 0) == 0
+    assert L.h3_gate_residual(P, P + (1 << 30), P, 0, 64, P + (2 << 30), 3, 0, None, 0, 0, 0) == blk.H3_OK
+
+
+def test_gemm_validation(lib):
+    L = blk.load()
+    A, W, C = P, P + (1 << 32), P + (2 << 32)
+    g = lambda **k: L.h3_gemm_bf16(k.get("A", A), k.get("lda", 5376), k.get("W", W), k.get("ldw", 5376),
+                                   k.get("C", C), k.get("ldc", 21504), k.get("M", 100), k.get("N", 21504),
+                                   k.get("K", 5376), k.get("dt", 0), 0)
+    assert g(dt=2) == blk.H3_ERR_DTYPE
+    assert g(A=0) == blk.H3_ERR_ARG
+    assert g(lda=100) == blk.H3_ERR_ARG
+    assert g(ldc=100) == blk.H3_ERR_ARG
+    assert g(K=5376 - 8, lda=5376 - 8, ldw=5376 - 8) == blk.H3_ERR_SHAPE   # bf16 K % 64
+    assert g(N=21500, ldc=21504) == blk.H3_ERR_SHAPE
+    assert g(A=A + 2) == blk.H3_ERR_ALIGN
+    assert g(lda=5380) == blk.H3_ERR_ALIGN
+    assert g(C=A + 1024) == blk.H3_ERR_ARG                                   # C overlaps A
+    assert g(M=-1) == blk.H3_ERR_ARG
+    assert g(M=1 << 31) == blk.H3_ERR_SHAPE
+
+
+def test_qknorm_rope_validation(lib):
+    L = blk.load()
+    segs = blk.segments(CFG2.segments)
+    q, k = P, P + 7168 * 2
+    def r(**kw):
+        a = dict(q=q, k=k, ld=21504, n=CFG2.n_tok, heads=56, hd=128, gq=None, gk=None, eps=1e-6, dt_=64, dh=32,
+                 dw=32, base=1e4, segs=segs, ns=len(CFG2.segments), dt=0)
+        a.update(kw)
+        return L.h3_qknorm_rope3d(a["q"], a["k"], a["ld"], a["n"], a["heads"], a["hd"], a["gq"], a["gk"], a["eps"],
+                                  a["dt_"], a["dh"], a["dw"], a["base"], a["segs"], a["ns"], a["dt"], 0)
+    assert r(dt=3) == blk.H3_ERR_DTYPE
+    assert r(hd=96) == blk.H3_ERR_SHAPE
+    assert r(dt_=63, dh=33) == blk.H3_ERR_SHAPE
+    assert r(dt_=64, dh=32, dw=30) == blk.H3_ERR_SHAPE
+    assert r(base=0.0) == blk.H3_ERR_ARG
+    assert r(ld=7000) == blk.H3_ERR_ARG
+    assert r(k=q + 128) == blk.H3_ERR_ARG             # k columns overlap q's
+    assert r(gq=P + 2) == blk.H3_ERR_ALIGN
+    assert r(ns=2) == blk.H3_ERR_SEGMENTS
+
+
+def test_attention_validation(lib):
+    L = blk.load()
+    q, k, v, o = P, P + 14336, P + 28672, P + (4 << 32)
+    def a(**kw):
+        x = dict(q=q, k=k, v=v, ld=21504, o=o, ldo=7168, n=25616, heads=56, hd=128, scale=0.088, lse=None, dt=0)
+        x.update(kw)
+        return L.h3_attention_fwd(x["q"], x["k"], x["v"], x["ld"], x["o"], x["ldo"], x["n"], x["heads"], x["hd"],
+                                  x["scale"], x["lse"], x["dt"], 0)
+    assert a(dt=9) == blk.H3_ERR_DTYPE
+    assert a(hd=32) == blk.H3_ERR_SHAPE
+    assert a(o=q) == blk.H3_ERR_ARG
+    assert a(ldo=100) == blk.H3_ERR_ARG
+    assert a(scale=float("inf")) == blk.H3_ERR_ARG
+    assert a(lse=P + 2) == blk.H3_ERR_ALIGN
+    assert a(ld=1 << 24) == blk.H3_ERR_SHAPE
+    assert a(q=q + 8) == blk.H3_ERR_ALIGN
+
+
+def test_swiglu_and_gate_validation(lib):
+    L = blk.load()
+    assert L.h3_swiglu(P, P + (1 << 32), 10, 12, 0, 0) == blk.H3_ERR_SHAPE
+    assert L.h3_swiglu(P, P + 64, 10, 64, 0, 0) == blk.H3_ERR_ARG          # h overlaps gu
+    assert L.h3_swiglu(P, P + (1 << 32), 10, 64, 4, 0) == blk.H3_ERR_DTYPE
+    segs = blk.segments(CFG1.segments)
+    x, y = P, P + (1 << 30)
+    assert L.h3_gate_residual(x, y, x + 64, 72, 192, P + (2 << 30), 3, 0, segs, 3, 1, 0) == blk.H3_ERR_ARG
+    assert L.h3_gate_residual(x, y, y, 72, 192, P + (2 << 30), 3, 0, segs, 3, 1, 0) == blk.H3_ERR_ARG
+    assert L.h3_gate_residual(x, y, x, 72, 191, P + (2 << 30), 3, 0, segs, 3, 1, 0) == blk.H3_ERR_SHAPE
+    assert L.h3_gate_residual(x, y, x, 72, 192, P + (2 << 30), 2, 0, segs, 3, 1, 0) == blk.H3_ERR_SEGMENTS
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine with no GPU (fake pointers)")
+def test_valid_arguments_without_a_device_report_hip_error(lib):
+    assert _adaln() == blk.H3_ERR_HIP
+    L = blk.load()
+    assert L.h3_swiglu(P, P + (1 << 32), 10, 64, 0, 0) == blk.H3_ERR_HIP

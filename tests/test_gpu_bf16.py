@@ -1,0 +1,202 @@
+"""GPU parity of the bf16 path against the fp64 oracle (tolerance 2e-2).
+
+* The 4 s 16:9 768p workload (25616 tokens, full width): every call checked
+  on sampled rows with the GPU's own inputs to that call, and the whole
+  block checked end to end on sampled rows (the oracle computes K and V for
+  every token and the rest for the sampled rows).
+* Ragged and degenerate sizes for the GEMM and attention tiles.
+* A peaked softmax (Q/K gains 4), permuted interval order, and run-to-run
+  bitwise determinism.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from video_audio_diffusion_amd import blk, inputs
+
+from gpu_util import TOL, assert_close, make_device, oracle_inputs, run_block_steps, widen
+
+pytestmark = pytest.mark.gpu
+C2 = inputs.CONFIGS[2]
+TB = TOL["bf16"]
+
+
+def _small(gamma=1.0, T=3):
+    """A narrow bf16 block with a ragged token count (117 tokens)."""
+    return inputs.BlockConfig(
+        name="ragged-bf16", index=11, dim=256, heads=2, head_dim=128, ffn=512, rope_split=(64, 32, 32),
+        rope_base=10000.0, dtype="bf16", gamma=gamma,
+        segments=inputs.pack([("text", 0, 7, 1, 1), ("audio", 2, 5, 1, 1), ("video", 1, T, 5, 7)]))
+
+
+@pytest.fixture(scope="module")
+def c2():
+    import torch
+    assert torch.cuda.is_available()
+    blk.load()
+    host = inputs.make_inputs(C2)
+    dev = make_device(C2, host)
+    print("[c2] running block", flush=True)
+    r = run_block_steps(C2, dev)
+    return host, dev, r, inputs.sample_rows(C2, n_random=384)
+
+
+def test_c2_each_call(c2):
+    host, dev, r, rows = c2
+    c = C2
+    t = oracle_inputs(c, {k: host[k] for k in ("mod", "gamma_q", "gamma_k", "w_o", "w_d")})
+    W = lambda k: widen(r[k], "bf16")
+    x = inputs.widen(host["x"][rows], "bf16")
+    mod = t["mod"]
+    I = c.inner
+    _, pos = oracle.token_table(c.segments, c.n_tok)
+    a = W("a")[rows]
+    assert_close("adaln_attn", a, oracle.adaln_modulate(x, mod, 0, c.segments, c.eps, rows=rows), TB)
+    wqkv = inputs.widen(host["w_qkv"], "bf16")
+    raw = W("qkv_raw")
+    assert_close("gemm_qkv", raw[rows], oracle.linear(a, wqkv), TB)
+    qkv = W("qkv")
+    for name, sl, gam in (("q", slice(0, I), t["gamma_q"]), ("k", slice(I, 2 * I), t["gamma_k"])):
+        ref = oracle.rope3d(oracle.qk_rmsnorm(raw[rows, sl], c.heads, c.head_dim, gam, c.eps), pos[rows],
+                            c.heads, c.head_dim, c.rope_split, c.rope_base)
+        assert_close("qknorm_rope_" + name, qkv[rows, sl], ref, TB)
+    arows = rows[:: max(1, len(rows) // 128)]
+    o_ref = oracle.attention(qkv[arows, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], c.heads, c.head_dim, c.scale,
+                             rows=arows)
+    assert_close("attention", W("o")[arows], o_ref, TB)
+    assert_close("gemm_o", W("y")[rows], oracle.linear(W("o")[rows], t["w_o"]), TB)
+    assert_close("gate_attn", W("x1")[rows], oracle.gate_residual(x, W("y")[rows], mod, 0, c.segments, rows=rows), TB)
+    a2 = W("a2")[rows]
+    assert_close("adaln_ffn", a2, oracle.adaln_modulate(W("x1")[rows], mod, 1, c.segments, c.eps, rows=rows), TB)
+    wgu = inputs.widen(host["w_gu"], "bf16")
+    assert_close("gemm_gu", W("gu")[rows], oracle.linear(a2, wgu), TB)
+    del wgu
+    assert_close("swiglu", W("h")[rows], oracle.swiglu(W("gu")[rows], c.ffn), TB)
+    assert_close("gemm_d", W("f")[rows], oracle.linear(W("h")[rows], t["w_d"]), TB)
+    assert_close("gate_ffn", W("out")[rows],
+                 oracle.gate_residual(W("x1")[rows], W("f")[rows], mod, 1, c.segments, rows=rows), TB)
+
+
+def test_c2_block_end_to_end(c2):
+    host, dev, r, rows = c2
+    rows = rows[:: max(1, len(rows) // 160)]
+    ref = oracle.block_forward(oracle_inputs(C2, host), C2, rows=rows)
+    got = widen(r["out"], "bf16")[rows]
+    x = inputs.widen(host["x"][rows], "bf16")
+    assert_close("block_out", got, ref["out"], TB)
+    assert_close("block_delta", got - x, ref["out"] - x, TB)
+    assert_close("block_o", widen(r["o"], "bf16")[rows], ref["o"], TB)
+
+
+def test_c2_deterministic(c2):
+    import torch
+    host, dev, r, rows = c2
+    r2 = run_block_steps(C2, dev)
+    for k in ("qkv", "o", "out"):
+        assert torch.equal(r[k], r2[k]), k
+
+
+@pytest.mark.parametrize("gamma", [1.0, 4.0])
+def test_small_ragged_block(gamma):
+    cfg = _small(gamma)
+    host = inputs.make_inputs(cfg)
+    dev = make_device(cfg, host)
+    r = run_block_steps(cfg, dev)
+    ref = oracle.block_forward(oracle_inputs(cfg, host), cfg)
+    x = inputs.widen(host["x"], "bf16")
+    got = widen(r["out"], "bf16")
+    assert_close(f"small_out_g{gamma}", got, ref["out"], TB)
+    assert_close(f"small_delta_g{gamma}", got - x, ref["out"] - x, TB)
+    assert_close(f"small_o_g{gamma}", widen(r["o"], "bf16"), ref["o"], TB)
+
+
+def test_permuted_intervals():
+    import torch
+    cfg = _small()
+    host = inputs.make_inputs(cfg)
+    dev = make_device(cfg, host)
+    base = run_block_steps(cfg, dev)["out"]
+    for order in ((2, 1, 0), (1, 2, 0)):
+        pcfg, rows = inputs.permuted(cfg, order)
+        xp = dev["x"][torch.from_numpy(rows).cuda()].contiguous()
+        got = run_block_steps(pcfg, dev, x=xp)["out"]
+        a, b = widen(got, "bf16"), widen(base, "bf16")[rows]
+        assert_close(f"permuted{order}", a, b, TB)
+
+
+def _rand(shape, seed):
+    return inputs.draw_rows(None, shape, seed, dtype="bf16")
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 64, 65, 255, 256, 257, 1000, 4097])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_ragged(n, hd):
+    import torch
+    from video_audio_diffusion_amd.block import device_inputs
+    H = 3
+    qkv_h = _rand((n, 3 * H * hd), 100 + n + hd)
+    qkv = device_inputs(None, {"qkv": qkv_h})["qkv"]
+    o = torch.empty(n, H * hd, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(H, n, dtype=torch.float32, device="cuda")
+    I = H * hd
+    blk.h3_attention_fwd(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], 3 * I, o, I, n, H, hd, hd ** -0.5, lse,
+                         blk.H3_BF16)
+    torch.cuda.synchronize()
+    f = inputs.widen(qkv_h, "bf16")
+    ref = oracle.attention(f[:, :I], f[:, I:2 * I], f[:, 2 * I:], H, hd, hd ** -0.5)
+    assert_close(f"attn n={n} hd={hd}", widen(o, "bf16"), ref, TB)
+    qh, kh = f[:, :I].reshape(n, H, hd), f[:, I:2 * I].reshape(n, H, hd)
+    s = np.einsum("ihd,jhd->hij", qh, kh) * hd ** -0.5
+    lref = s.max(-1) + np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1))
+    np.testing.assert_allclose(lse.cpu().numpy(), lref, rtol=1e-3, atol=1e-3)
+
+
+def test_attention_peaked_full_width():
+    """56 heads x 128 over 4097 tokens with logits of std about 16."""
+    import torch
+    from video_audio_diffusion_amd.block import device_inputs
+    n, H, hd = 4097, 56, 128
+    I = H * hd
+    g = np.random.Generator(np.random.PCG64(77))
+    qkv32 = g.standard_normal((n, 3 * I), dtype=np.float32)
+    qkv32[:, :2 * I] *= 4.0 / np.sqrt(np.float32(1.0))   # q.k/sqrt(d) has std 16
+    qkv_h = inputs.f32_to_bf16_bits(qkv32)
+    qkv = device_inputs(None, {"qkv": qkv_h})["qkv"]
+    o = torch.empty(n, I, dtype=torch.bfloat16, device="cuda")
+    blk.h3_attention_fwd(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], 3 * I, o, I, n, H, hd, hd ** -0.5, None,
+                         blk.H3_BF16)
+    torch.cuda.synchronize()
+    f = inputs.widen(qkv_h, "bf16")
+    rows = np.array([0, 1, 255, 256, 2048, 4095, 4096])
+    ref = oracle.attention(f[rows, :I], f[:, I:2 * I], f[:, 2 * I:], H, hd, hd ** -0.5, rows=rows)
+    assert_close("attn_peaked", widen(o, "bf16")[rows], ref, TB)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (255, 200, 192), (257, 264, 576), (1000, 512, 64),
+                                   (513, 1032, 1024)])
+def test_gemm_ragged(M, N, K):
+    import torch
+    from video_audio_diffusion_amd.block import device_inputs
+    a_h, w_h = _rand((M, K), 5 + M), _rand((N, K), 6 + N)
+    d = device_inputs(None, {"a": a_h, "w": w_h})
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    blk.h3_gemm_bf16(d["a"], K, d["w"], K, c, N, M, N, K, blk.H3_BF16)
+    torch.cuda.synchronize()
+    ref = oracle.linear(inputs.widen(a_h, "bf16"), inputs.widen(w_h, "bf16"))
+    assert_close(f"gemm {M}x{N}x{K}", widen(c, "bf16"), ref, TB)
+
+
+def test_gemm_strided_views():
+    """Row strides wider than the rows (the o -> y projection reads a view)."""
+    import torch
+    from video_audio_diffusion_amd.block import device_inputs
+    M, N, K = 300, 264, 128
+    a_h, w_h = _rand((M, 3 * K), 9), _rand((N, 2 * K), 10)
+    d = device_inputs(None, {"a": a_h, "w": w_h})
+    c = torch.zeros(M, 2 * N, dtype=torch.bfloat16, device="cuda")
+    blk.h3_gemm_bf16(d["a"][:, K:], 3 * K, d["w"][:, K:], 2 * K, c[:, N:], 2 * N, M, N, K, blk.H3_BF16)
+    torch.cuda.synchronize()
+    ref = oracle.linear(inputs.widen(a_h, "bf16")[:, K:2 * K], inputs.widen(w_h, "bf16")[:, K:])
+    got = widen(c, "bf16")
+    assert_close("gemm strided", got[:, N:], ref, TB)
+    assert np.all(got[:, :N] == 0)            # nothing written outside C

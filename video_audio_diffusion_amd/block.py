@@ -1,0 +1,115 @@
+"""One H3-Omni-Transformer block forward as eleven libh3blk calls.
+
+This driver only allocates device buffers (torch) and issues the calls in
+the block order of the "MiniMax-H3: native audio-video joint generation"
+notes, section 3; every step runs in the library's kernels.
+
+Buffers (row-major, tokens as rows):
+    a   [N, D]    modulated norm output (reused for a2)
+    qkv [N, 3I]   [q heads | k heads | v heads]; q and k are normed and
+                  rotated in place
+    o   [N, I]    attention output
+    y   [N, D]    projection output (reused for the FFN down projection)
+    x1  [N, D]    residual after attention
+    gu  [N, 2F]   [gate | up]
+    h   [N, F]    SwiGLU output
+    out [N, D]
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+from . import blk
+
+
+@dataclass
+class BlockWeights:
+    w_qkv: object   # [3I, D]
+    w_o: object     # [D, I]
+    w_gu: object    # [2F, D]
+    w_d: object     # [D, F]
+    mod: object     # fp32 [n_sets, 6, D]
+    gamma_q: object = None   # fp32 [head_dim] or None
+    gamma_k: object = None
+
+
+class H3Block:
+    STEPS = ("adaln_attn", "gemm_qkv", "qknorm_rope", "attention", "gemm_o", "gate_attn",
+             "adaln_ffn", "gemm_gu", "swiglu", "gemm_d", "gate_ffn")
+
+    def __init__(self, cfg, weights: BlockWeights, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.w = weights
+        self.dt = blk.H3_BF16 if cfg.dtype == "bf16" else blk.H3_F32
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        N, D, I, F = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn
+        e = lambda *s: torch.empty(*s, dtype=tdt, device=device)
+        self.buf: Dict[str, object] = {"a": e(N, D), "qkv": e(N, 3 * I), "o": e(N, I), "y": e(N, D),
+                                       "x1": e(N, D), "gu": e(N, 2 * F), "h": e(N, F), "out": e(N, D)}
+        self.segs = blk.segments(cfg.segments)
+        self.n_segs = len(cfg.segments)
+        self.n_sets = int(weights.mod.shape[0])
+
+    def forward(self, x, stream: Optional[int] = None, events=None):
+        """Run the block on x [N, D]; returns the `out` buffer.  With `events`
+        (a list of 12 torch.cuda.Event), event i is recorded before step i."""
+        c, b, w = self.cfg, self.buf, self.w
+        N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
+        dt, segs, ns, nset = self.dt, self.segs, self.n_segs, self.n_sets
+        st = blk.current_stream() if stream is None else stream
+        qkv = b["qkv"]
+        q, k, v = qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:]
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+
+        rec(0)
+        blk.h3_adaln_modulate(x, b["a"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, c.eps, dt, st)
+        rec(1)
+        blk.h3_gemm_bf16(b["a"], D, w.w_qkv, D, qkv, 3 * I, N, 3 * I, D, dt, st)
+        rec(2)
+        blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base,
+                             segs, ns, dt, st)
+        rec(3)
+        blk.h3_attention_fwd(q, k, v, 3 * I, b["o"], I, N, H, d, c.scale, None, dt, st)
+        rec(4)
+        blk.h3_gemm_bf16(b["o"], I, w.w_o, I, b["y"], D, N, D, I, dt, st)
+        rec(5)
+        blk.h3_gate_residual(x, b["y"], b["x1"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, dt, st)
+        rec(6)
+        blk.h3_adaln_modulate(b["x1"], b["a"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, c.eps, dt, st)
+        rec(7)
+        blk.h3_gemm_bf16(b["a"], D, w.w_gu, D, b["gu"], 2 * F, N, 2 * F, D, dt, st)
+        rec(8)
+        blk.h3_swiglu(b["gu"], b["h"], N, F, dt, st)
+        rec(9)
+        blk.h3_gemm_bf16(b["h"], F, w.w_d, F, b["y"], D, N, D, F, dt, st)
+        rec(10)
+        blk.h3_gate_residual(b["x1"], b["y"], b["out"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, dt, st)
+        rec(11)
+        return b["out"]
+
+
+def device_inputs(cfg, host: Dict, device="cuda"):
+    """Host arrays from `inputs.make_inputs` -> device tensors (bf16 bits are
+    reinterpreted, not converted)."""
+    import numpy as np
+    import torch
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    out = {k: dev(v) for k, v in host.items()}
+    return out
+
+
+def host_array(t, dtype: str):
+    """Device tensor -> host numpy (bf16 kept as uint16 bits)."""
+    import numpy as np
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()

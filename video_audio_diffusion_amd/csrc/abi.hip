@@ -1,0 +1,209 @@
+// The C ABI of libh3blk: argument validation, then one launch per call.
+// Everything is checked on the host before anything is enqueued, so an
+// error code always means that no work ran and no output was touched.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/h3blk.h"
+#include "launch.h"
+
+using namespace h3;
+
+namespace {
+
+constexpr int64_t kMaxTok = (int64_t)1 << 31;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool valid_dt(h3_dtype dt) { return dt == H3_BF16 || dt == H3_F32; }
+inline int esize(h3_dtype dt) { return dt == H3_BF16 ? 2 : 4; }
+inline bool valid_branch(h3_branch br) { return br == H3_BRANCH_ATTN || br == H3_BRANCH_FFN; }
+
+// Byte range [lo, hi) spanned by a strided [rows][cols] view.
+struct Span {
+    uintptr_t lo, hi;
+};
+inline Span span(const void* p, int64_t rows, int64_t cols, int64_t ld, int es) {
+    const uintptr_t lo = (uintptr_t)p;
+    if (rows <= 0 || cols <= 0) return {lo, lo};
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * es)};
+}
+inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Intervals must be sorted, contiguous, non-empty, cover [0, n_tok) and
+// have len == T*H*W; mod_set must index the modulation table when one is
+// used (n_sets > 0).
+h3_status build_segs(const h3_segment* segs, int32_t n_segs, int64_t n_tok, int32_t n_sets, SegTable* tab) {
+    if (n_segs < 0 || n_segs > H3_MAX_SEGMENTS) return H3_ERR_SEGMENTS;
+    if (n_segs > 0 && !segs) return H3_ERR_ARG;
+    memset(tab, 0, sizeof(*tab));
+    int64_t pos = 0;
+    for (int i = 0; i < n_segs; ++i) {
+        const h3_segment& s = segs[i];
+        if (s.start != pos || s.len < 1) return H3_ERR_SEGMENTS;
+        if (s.T < 1 || s.H < 1 || s.W < 1 || s.t0 < 0 || s.h0 < 0 || s.w0 < 0) return H3_ERR_SEGMENTS;
+        if ((int64_t)s.T * s.H * s.W != s.len) return H3_ERR_SEGMENTS;
+        if ((int64_t)s.H * s.W > INT32_MAX) return H3_ERR_SEGMENTS;
+        if ((int64_t)s.t0 + s.T > INT32_MAX || (int64_t)s.h0 + s.H > INT32_MAX ||
+            (int64_t)s.w0 + s.W > INT32_MAX)
+            return H3_ERR_SEGMENTS;
+        if (n_sets > 0 && (s.mod_set < 0 || s.mod_set >= n_sets)) return H3_ERR_SEGMENTS;
+        pos += s.len;
+        if (pos > n_tok) return H3_ERR_SEGMENTS;
+        tab->s[i] = SegDev{(int32_t)s.start, s.mod_set, s.H * s.W, s.W, s.H, s.t0, s.h0, s.w0};
+    }
+    if (pos != n_tok) return H3_ERR_SEGMENTS;
+    tab->n = n_segs;
+    return H3_OK;
+}
+
+inline h3_status hip_status(hipError_t e) { return e == hipSuccess ? H3_OK : H3_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* h3_status_str(h3_status s) {
+    switch (s) {
+        case H3_OK: return "ok";
+        case H3_ERR_ARG: return "invalid argument";
+        case H3_ERR_SEGMENTS: return "invalid interval table";
+        case H3_ERR_DTYPE: return "unsupported dtype";
+        case H3_ERR_ALIGN: return "misaligned pointer or row stride";
+        case H3_ERR_SHAPE: return "unsupported size";
+        case H3_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim, const float* mod,
+                            int32_t n_sets, h3_branch br, const h3_segment* segs, int32_t n_segs,
+                            float eps, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!x || !y || !mod || n_tok < 0 || n_sets < 1 || !valid_branch(br) || !(eps >= 0.f) || !isfinite(eps))
+        return H3_ERR_ARG;
+    if (n_tok >= kMaxTok || dim < 8 || dim % 8 || dim > kWave * kRowMaxVecPerLane * (16 / esize(dt)))
+        return H3_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(mod)) return H3_ERR_ALIGN;
+    if (overlap(span(x, n_tok, dim, dim, esize(dt)), span(y, n_tok, dim, dim, esize(dt)))) return H3_ERR_ARG;
+    SegTable tab;
+    const h3_status st = build_segs(segs, n_segs, n_tok, n_sets, &tab);
+    if (st != H3_OK) return st;
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_adaln(dt == H3_BF16, x, y, (int32_t)n_tok, dim, mod, (int32_t)br, tab, eps,
+                                   (hipStream_t)stream));
+}
+
+h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+                       int64_t M, int32_t N, int32_t K, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!A || !W || !C || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
+    const int es = esize(dt);
+    if (lda < K || ldw < K || ldc < N) return H3_ERR_ARG;
+    if (M >= kMaxTok || N % 8 || K % (dt == H3_BF16 ? 64 : 32)) return H3_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (lda * es) % 16 || (ldw * es) % 16 ||
+        (ldc * es) % 16)
+        return H3_ERR_ALIGN;
+    const Span c = span(C, M, N, ldc, es);
+    if (overlap(c, span(A, M, K, lda, es)) || overlap(c, span(W, N, K, ldw, es))) return H3_ERR_ARG;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, (hipStream_t)stream));
+}
+
+h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok, int32_t heads, int32_t head_dim,
+                           const float* gamma_q, const float* gamma_k, float eps, int32_t d_t, int32_t d_h,
+                           int32_t d_w, float rope_base, const h3_segment* segs, int32_t n_segs,
+                           h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!q || !k || n_tok < 0 || heads < 1 || !(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) ||
+        !isfinite(rope_base))
+        return H3_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
+    if (d_t < 0 || d_h < 0 || d_w < 0 || d_t % 2 || d_h % 2 || d_w % 2 || d_t + d_h + d_w != head_dim)
+        return H3_ERR_SHAPE;
+    if (n_tok >= kMaxTok) return H3_ERR_SHAPE;
+    const int es = esize(dt);
+    const int64_t width = (int64_t)heads * head_dim;
+    if (ld < width) return H3_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || (ld * es) % 16 || ((uintptr_t)gamma_q & 3) ||
+        ((uintptr_t)gamma_k & 3))
+        return H3_ERR_ALIGN;
+    if (overlap(span(q, n_tok, width, ld, es), span(k, n_tok, width, ld, es))) {
+        // q and k may be interleaved column blocks of one buffer, never the same columns
+        const intptr_t diff = (intptr_t)((uintptr_t)k - (uintptr_t)q) / es;
+        const intptr_t rem = ((diff % ld) + ld) % ld;
+        if (rem < width || ld - rem < width) return H3_ERR_ARG;
+    }
+    SegTable tab;
+    const h3_status st = build_segs(segs, n_segs, n_tok, 0, &tab);
+    if (st != H3_OK) return st;
+    if (n_tok == 0) return H3_OK;
+    // per-pair rotation table, exact in double: frequency base^(-2j/d_axis)
+    RopeTable rt;
+    memset(&rt, 0, sizeof(rt));
+    const int split[3] = {d_t, d_h, d_w};
+    int axis = 0, first = 0;
+    for (int p = 0; p < head_dim / 2; ++p) {
+        while (2 * p >= first + split[axis]) first += split[axis++];
+        const int j = p - first / 2;
+        rt.axis[p] = (int8_t)axis;
+        rt.inv_freq[p] = pow((double)rope_base, -2.0 * j / (double)split[axis]);
+    }
+    return hip_status(launch_qknorm_rope(dt == H3_BF16, q, k, ld, (int32_t)n_tok, heads, head_dim, gamma_q,
+                                         gamma_k, eps, rt, tab, (hipStream_t)stream));
+}
+
+h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o, int64_t ld_o,
+                           int64_t n_tok, int32_t heads, int32_t head_dim, float scale, float* lse,
+                           h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!q || !k || !v || !o || n_tok < 0 || heads < 1 || !isfinite(scale)) return H3_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
+    const int es = esize(dt);
+    const int64_t width = (int64_t)heads * head_dim;
+    if (ld_qkv < width || ld_o < width) return H3_ERR_ARG;
+    // the kernel addresses a 64-key tile with 32-bit byte offsets
+    if (n_tok >= kMaxTok || ld_qkv * es >= ((int64_t)1 << 25)) return H3_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (ld_qkv * es) % 16 ||
+        (ld_o * es) % 16 || ((uintptr_t)lse & 3))
+        return H3_ERR_ALIGN;
+    const Span so = span(o, n_tok, width, ld_o, es);
+    if (overlap(so, span(q, n_tok, width, ld_qkv, es)) || overlap(so, span(k, n_tok, width, ld_qkv, es)) ||
+        overlap(so, span(v, n_tok, width, ld_qkv, es)))
+        return H3_ERR_ARG;
+    if (lse && overlap(span(lse, 1, (int64_t)heads * n_tok, 0, 4), so)) return H3_ERR_ARG;
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_attention(dt == H3_BF16, q, k, v, ld_qkv, o, ld_o, (int32_t)n_tok, heads, head_dim,
+                                       scale, lse, (hipStream_t)stream));
+}
+
+h3_status h3_swiglu(const void* gu, void* h, int64_t n_tok, int32_t F, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!gu || !h || n_tok < 0 || F < 1) return H3_ERR_ARG;
+    if (F % 8 || n_tok >= kMaxTok) return H3_ERR_SHAPE;
+    if (!aligned16(gu) || !aligned16(h)) return H3_ERR_ALIGN;
+    const int es = esize(dt);
+    if (overlap(span(gu, n_tok, 2 * (int64_t)F, 2 * (int64_t)F, es), span(h, n_tok, F, F, es))) return H3_ERR_ARG;
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_swiglu(dt == H3_BF16, gu, h, n_tok, F, (hipStream_t)stream));
+}
+
+h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_tok, int32_t dim,
+                           const float* mod, int32_t n_sets, h3_branch br, const h3_segment* segs,
+                           int32_t n_segs, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!x || !y || !out || !mod || n_tok < 0 || n_sets < 1 || !valid_branch(br)) return H3_ERR_ARG;
+    if (dim < 8 || dim % 8 || n_tok >= kMaxTok) return H3_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(out) || !aligned16(mod)) return H3_ERR_ALIGN;
+    const int es = esize(dt);
+    const Span so = span(out, n_tok, dim, dim, es);
+    if (overlap(so, span(y, n_tok, dim, dim, es))) return H3_ERR_ARG;
+    if (out != x && overlap(so, span(x, n_tok, dim, dim, es))) return H3_ERR_ARG;
+    SegTable tab;
+    const h3_status st = build_segs(segs, n_segs, n_tok, n_sets, &tab);
+    if (st != H3_OK) return st;
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_gate_residual(dt == H3_BF16, x, y, out, (int32_t)n_tok, dim, mod, (int32_t)br, tab,
+                                           (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+// Bandwidth-bound passes of the H3 block: modulated RMSNorm, modality-gated
+// residual, SwiGLU, and per-head QK RMSNorm fused with 3-D MM-RoPE.
+//
+// All of them stream 16-byte vectors with consecutive lanes on consecutive
+// addresses and keep every value in fp32 between the load and the one
+// rounding at the store.  Row kernels give one wavefront to one token row so
+// the interval lookup and the row reduction are per-wave scalars.
+#include "launch.h"
+
+namespace h3 {
+
+// --------------------------------------------------------------------------
+// Modulated RMSNorm (one wavefront per row, the row held in registers).
+//   y = x * rsqrt(mean(x^2) + eps) * (1 + scale[set]) + shift[set]
+template <typename T, int VPL>
+__global__ __launch_bounds__(256) void adaln_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                    int32_t n, int32_t dim,
+                                                    const float* __restrict__ mod, int32_t br,
+                                                    SegTable tab, float eps) {
+    constexpr int N = Vec<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    const int nv = dim / N;
+    const char* xr = reinterpret_cast<const char*>(x + (int64_t)row * dim);
+    char* yr = reinterpret_cast<char*>(y + (int64_t)row * dim);
+    float v[VPL][N];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int j = lane + kWave * i;
+        if (j < nv) {
+            Vec<T>::load(xr + 16 * j, v[i]);
+#pragma unroll
+            for (int e = 0; e < N; ++e) ss += v[i][e] * v[i][e];
+        }
+    }
+    ss = sum_lanes<kWave>(ss);
+    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)dim + eps);
+    const int s = find_seg(tab, row);
+    const float* shift = mod + ((int64_t)tab.s[s].mod_set * 6 + 3 * br) * dim;
+    const float* scale = shift + dim;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int j = lane + kWave * i;
+        if (j < nv) {
+            float o[N];
+#pragma unroll
+            for (int e = 0; e < N; e += 4) {
+                const f32x4 sh = *reinterpret_cast<const f32x4*>(shift + j * N + e);
+                const f32x4 sc = *reinterpret_cast<const f32x4*>(scale + j * N + e);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[e + u] = v[i][e + u] * rstd * (1.0f + sc[u]) + sh[u];
+            }
+            Vec<T>::store(yr + 16 * j, o);
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Modality-gated residual: out = x + gate[set] * y (one wavefront per row).
+template <typename T>
+__global__ __launch_bounds__(256) void gate_residual_kernel(const T* x, const T* __restrict__ y, T* out,
+                                                            int32_t n, int32_t dim,
+                                                            const float* __restrict__ mod, int32_t br,
+                                                            SegTable tab) {
+    constexpr int N = Vec<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    const int nv = dim / N;
+    const int s = find_seg(tab, row);
+    const float* gate = mod + ((int64_t)tab.s[s].mod_set * 6 + 3 * br + 2) * dim;
+    const char* xr = reinterpret_cast<const char*>(x + (int64_t)row * dim);
+    const char* yr = reinterpret_cast<const char*>(y + (int64_t)row * dim);
+    char* orow = reinterpret_cast<char*>(out + (int64_t)row * dim);
+    for (int j = lane; j < nv; j += kWave) {
+        float a[N], b[N], o[N];
+        Vec<T>::load(xr + 16 * j, a);
+        Vec<T>::load(yr + 16 * j, b);
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(gate + j * N + e);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[e + u] = a[e + u] + g[u] * b[e + u];
+        }
+        Vec<T>::store(orow + 16 * j, o);
+    }
+}
+
+// --------------------------------------------------------------------------
+// SwiGLU: h = g / (1 + exp(-g)) * u over [gate | up] rows.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const T* __restrict__ gu, T* __restrict__ h,
+                                                     int64_t n, int32_t F) {
+    constexpr int N = Vec<T>::N;
+    const int64_t fv = F / N;
+    const int64_t total = n * fv;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = idx / fv;
+        const int64_t c = idx - row * fv;
+        const T* g = gu + row * 2 * F + c * N;
+        float a[N], b[N], o[N];
+        Vec<T>::load(g, a);
+        Vec<T>::load(g + F, b);
+#pragma unroll
+        for (int e = 0; e < N; ++e) o[e] = a[e] / (1.0f + __expf(-a[e])) * b[e];
+        Vec<T>::store(h + row * F + c * N, o);
+    }
+}
+
+// --------------------------------------------------------------------------
+// Per-head RMSNorm of Q and K, then 3-D MM-RoPE, in place.  One workgroup
+// per token: the token's (cos, sin) per pair are computed once into LDS and
+// reused by all 2*heads head vectors; LPH lanes share one head vector.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(T* q, T* k, int64_t ld, int32_t n,
+                                                          int32_t heads,
+                                                          const float* __restrict__ gq,
+                                                          const float* __restrict__ gk, float eps,
+                                                          RopeTable rt, SegTable tab) {
+    constexpr int N = Vec<T>::N;
+    constexpr int LPH = HD / N;           // lanes per head vector
+    constexpr int GROUPS = 256 / LPH;     // head vectors per round
+    __shared__ f32x2 cs[HD / 2];
+    const int row = blockIdx.x;
+    if (row >= n) return;                 // uniform for the workgroup
+    if (threadIdx.x < HD / 2) {
+        const int p = threadIdx.x;
+        const int s = find_seg(tab, row);
+        const SegDev& sg = tab.s[s];
+        const int l = row - sg.start;
+        const int axis = rt.axis[p];
+        const int pos = axis == 0 ? sg.t0 + l / sg.HW : axis == 1 ? sg.h0 + (l / sg.W) % sg.H
+                                                                  : sg.w0 + l % sg.W;
+        double sn, c;
+        sincos((double)pos * rt.inv_freq[p], &sn, &c);
+        cs[p] = (f32x2){(float)c, (float)sn};
+    }
+    __syncthreads();
+    const int sub = threadIdx.x % LPH;
+    const int grp = threadIdx.x / LPH;
+    for (int hv = grp; hv < 2 * heads; hv += GROUPS) {
+        const bool isq = hv < heads;
+        T* base = (isq ? q : k) + (int64_t)row * ld + (int64_t)(isq ? hv : hv - heads) * HD + sub * N;
+        const float* gamma = isq ? gq : gk;
+        float v[N];
+        Vec<T>::load(base, v);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < N; ++e) ss += v[e] * v[e];
+        ss = sum_lanes<LPH>(ss);
+        const float rstd = 1.0f / __builtin_sqrtf(ss / (float)HD + eps);
+#pragma unroll
+        for (int e = 0; e < N; ++e) v[e] *= rstd * (gamma ? gamma[sub * N + e] : 1.0f);
+#pragma unroll
+        for (int e = 0; e < N; e += 2) {
+            const f32x2 t = cs[(sub * N + e) / 2];
+            const float u0 = v[e], u1 = v[e + 1];
+            v[e] = u0 * t.x - u1 * t.y;
+            v[e + 1] = u0 * t.y + u1 * t.x;
+        }
+        Vec<T>::store(base, v);
+    }
+}
+
+// --------------------------------------------------------------------------
+// launchers
+
+template <typename T, int VPL>
+static hipError_t adaln_t(const void* x, void* y, int32_t n, int32_t dim, const float* mod, int32_t br,
+                          const SegTable& tab, float eps, hipStream_t st) {
+    adaln_kernel<T, VPL><<<(n + 3) / 4, 256, 0, st>>>((const T*)x, (T*)y, n, dim, mod, br, tab, eps);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t adaln_dispatch(const void* x, void* y, int32_t n, int32_t dim, const float* mod,
+                                 int32_t br, const SegTable& tab, float eps, hipStream_t st) {
+    const int per_lane = (dim / Vec<T>::N + kWave - 1) / kWave;
+    if (per_lane <= 1) return adaln_t<T, 1>(x, y, n, dim, mod, br, tab, eps, st);
+    if (per_lane <= 2) return adaln_t<T, 2>(x, y, n, dim, mod, br, tab, eps, st);
+    if (per_lane <= 4) return adaln_t<T, 4>(x, y, n, dim, mod, br, tab, eps, st);
+    if (per_lane <= 8) return adaln_t<T, 8>(x, y, n, dim, mod, br, tab, eps, st);
+    if (per_lane <= 12) return adaln_t<T, 12>(x, y, n, dim, mod, br, tab, eps, st);
+    return adaln_t<T, kRowMaxVecPerLane>(x, y, n, dim, mod, br, tab, eps, st);
+}
+
+hipError_t launch_adaln(bool bf, const void* x, void* y, int32_t n, int32_t dim, const float* mod,
+                        int32_t br, const SegTable& tab, float eps, hipStream_t st) {
+    return bf ? adaln_dispatch<bf16>(x, y, n, dim, mod, br, tab, eps, st)
+              : adaln_dispatch<float>(x, y, n, dim, mod, br, tab, eps, st);
+}
+
+hipError_t launch_gate_residual(bool bf, const void* x, const void* y, void* out, int32_t n,
+                                int32_t dim, const float* mod, int32_t br, const SegTable& tab,
+                                hipStream_t st) {
+    const int blocks = (n + 3) / 4;
+    if (bf)
+        gate_residual_kernel<bf16><<<blocks, 256, 0, st>>>((const bf16*)x, (const bf16*)y, (bf16*)out,
+                                                           n, dim, mod, br, tab);
+    else
+        gate_residual_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, (const float*)y,
+                                                            (float*)out, n, dim, mod, br, tab);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(bool bf, const void* gu, void* h, int64_t n, int32_t F, hipStream_t st) {
+    const int64_t total = n * (F / (bf ? 8 : 4));
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;   // grid-stride beyond 64 workgroups per CU
+    if (bf)
+        swiglu_kernel<bf16><<<(unsigned)blocks, 256, 0, st>>>((const bf16*)gu, (bf16*)h, n, F);
+    else
+        swiglu_kernel<float><<<(unsigned)blocks, 256, 0, st>>>((const float*)gu, (float*)h, n, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope(bool bf, void* q, void* k, int64_t ld, int32_t n, int32_t heads,
+                              int32_t hd, const float* gq, const float* gk, float eps,
+                              const RopeTable& rt, const SegTable& tab, hipStream_t st) {
+    if (bf) {
+        if (hd == 128)
+            qknorm_rope_kernel<bf16, 128><<<n, 256, 0, st>>>((bf16*)q, (bf16*)k, ld, n, heads, gq, gk,
+                                                             eps, rt, tab);
+        else
+            qknorm_rope_kernel<bf16, 64><<<n, 256, 0, st>>>((bf16*)q, (bf16*)k, ld, n, heads, gq, gk,
+                                                            eps, rt, tab);
+    } else {
+        if (hd == 128)
+            qknorm_rope_kernel<float, 128><<<n, 256, 0, st>>>((float*)q, (float*)k, ld, n, heads, gq,
+                                                              gk, eps, rt, tab);
+        else
+            qknorm_rope_kernel<float, 64><<<n, 256, 0, st>>>((float*)q, (float*)k, ld, n, heads, gq,
+                                                             gk, eps, rt, tab);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,35 @@
+// Internal launchers of libh3blk (host side).  The C ABI in abi.hip checks
+// every argument and then calls exactly one of these.
+#pragma once
+
+#include "common.h"
+
+namespace h3 {
+
+// Per-pair RoPE table: pair p of a head (elements 2p, 2p+1) turns with
+// the position on axis[p] (0 = t, 1 = h, 2 = w) at frequency inv_freq[p].
+struct RopeTable {
+    double inv_freq[64];
+    int8_t axis[64];
+};
+
+hipError_t launch_adaln(bool bf, const void* x, void* y, int32_t n, int32_t dim,
+                        const float* mod, int32_t br, const SegTable& tab, float eps,
+                        hipStream_t st);
+hipError_t launch_gate_residual(bool bf, const void* x, const void* y, void* out, int32_t n,
+                                int32_t dim, const float* mod, int32_t br, const SegTable& tab,
+                                hipStream_t st);
+hipError_t launch_swiglu(bool bf, const void* gu, void* h, int64_t n, int32_t F, hipStream_t st);
+hipError_t launch_qknorm_rope(bool bf, void* q, void* k, int64_t ld, int32_t n, int32_t heads,
+                              int32_t hd, const float* gq, const float* gk, float eps,
+                              const RopeTable& rt, const SegTable& tab, hipStream_t st);
+hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                       int64_t ldc, int64_t M, int32_t N, int32_t K, hipStream_t st);
+hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v, int64_t ld_qkv,
+                            void* o, int64_t ld_o, int32_t n, int32_t heads, int32_t hd,
+                            float scale, float* lse, hipStream_t st);
+
+// Largest row width (elements) the one-wave-per-row kernels hold in registers.
+constexpr int kRowMaxVecPerLane = 16;
+
+}  // namespace h3

@@ -32,6 +32,7 @@ bf16 with round-to-nearest-even; they are held as uint16 bit patterns.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field, replace
 from typing import Dict, List, Sequence, Tuple
 
@@ -198,16 +199,42 @@ def store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 # ---------------------------------------------------------------- draws
 
-def rng_for(cfg_index: int, tensor: str) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(1000 * cfg_index + TENSOR_IDS[tensor]))
+_CHUNK = 1 << 22          # elements per independently seeded chunk
 
 
-def draw(cfg_index: int, tensor: str, shape, std: float = 1.0) -> np.ndarray:
-    g = rng_for(cfg_index, tensor)
-    a = g.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        a *= np.float32(std)
-    return a
+def _fill_normal(out: np.ndarray, seed: int, std: float, dtype: str) -> None:
+    """Fill `out` (flat view) with N(0, std^2) draws: chunk c of 2^22 elements
+    comes from PCG64(SeedSequence([seed, c])), so chunks can be drawn by
+    several threads and the result does not depend on the thread count."""
+    import concurrent.futures as cf
+
+    flat = out.reshape(-1)
+
+    def one(c):
+        lo = c * _CHUNK
+        hi = min(flat.size, lo + _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, c])))
+        a = g.standard_normal(size=hi - lo, dtype=np.float32)
+        if std != 1.0:
+            a *= np.float32(std)
+        flat[lo:hi] = f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+    n_chunks = (flat.size + _CHUNK - 1) // _CHUNK
+    workers = min(16, os.cpu_count() or 1, max(1, n_chunks))
+    if workers == 1:
+        for c in range(n_chunks):
+            one(c)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(n_chunks)))
+
+
+def draw(cfg_index: int, tensor: str, shape, std: float = 1.0, dtype: str = "f32") -> np.ndarray:
+    """Seeded N(0, std^2) tensor in the stored representation of `dtype`
+    (seed 1000 * workload index + tensor id)."""
+    out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    _fill_normal(out, 1000 * cfg_index + TENSOR_IDS[tensor], std, dtype)
+    return out
 
 
 def make_inputs(cfg: BlockConfig, tensors: Sequence[str] = tuple(TENSOR_IDS)) -> Dict[str, np.ndarray]:
@@ -219,8 +246,7 @@ def make_inputs(cfg: BlockConfig, tensors: Sequence[str] = tuple(TENSOR_IDS)) ->
     out: Dict[str, np.ndarray] = {}
     for name in tensors:
         shape, std = shapes[name]
-        a = draw(cfg.index, name, shape, std)
-        out[name] = a if name == "mod" else store(a, cfg.dtype)
+        out[name] = draw(cfg.index, name, shape, std, "f32" if name == "mod" else cfg.dtype)
     out["gamma_q"] = np.full(cfg.head_dim, cfg.gamma, dtype=np.float32)
     out["gamma_k"] = np.full(cfg.head_dim, cfg.gamma, dtype=np.float32)
     return out
@@ -228,9 +254,9 @@ def make_inputs(cfg: BlockConfig, tensors: Sequence[str] = tuple(TENSOR_IDS)) ->
 
 def draw_rows(cfg: BlockConfig, shape, seed: int, dtype: str = None) -> np.ndarray:
     """Extra seeded N(0,1) tensors (per-call parity inputs, peaked variants)."""
-    g = np.random.Generator(np.random.PCG64(seed))
-    a = g.standard_normal(size=shape, dtype=np.float32)
-    return store(a, dtype or cfg.dtype)
+    out = np.empty(shape, dtype=np.uint16 if (dtype or cfg.dtype) == "bf16" else np.float32)
+    _fill_normal(out, seed, 1.0, dtype or cfg.dtype)
+    return out
 
 
 def sample_rows(cfg: BlockConfig, n_random: int = 2048, seed: int = 7) -> np.ndarray:
