@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (1-4)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget; 0 skips it")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget; 0 skips it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

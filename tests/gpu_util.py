@@ -25,6 +25,22 @@ def assert_close(name, got, ref, tol):
     assert e_max <= tol and e_f <= tol, f"{name}: e_max={e_max:.3e} e_F={e_f:.3e} > {tol}"
 
 
+def assert_delta_close(name, got_out, ref_out, x, tol, dtype):
+    """Parity of the residual-branch contribution out - x.  The output is
+    stored in `dtype`, so each element may differ from the exact value by up
+    to one spacing of that format at |out| before the branch error counts
+    (2^-8 relative for bf16, 2^-23 for fp32)."""
+    got_out, ref_out, x = (np.asarray(a, dtype=np.float64) for a in (got_out, ref_out, x))
+    unit = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    d = np.abs((got_out - x) - (ref_out - x))
+    excess = np.maximum(d - unit * np.abs(ref_out), 0.0)
+    ref_d = ref_out - x
+    e_max = excess.max() / np.abs(ref_d).max()
+    e_f = np.linalg.norm(excess) / np.linalg.norm(ref_d)
+    print(f"  {name}: e_max={e_max:.3e} e_F={e_f:.3e} beyond output rounding (tol {tol:g})", flush=True)
+    assert e_max <= tol and e_f <= tol, f"{name}: e_max={e_max:.3e} e_F={e_f:.3e} > {tol}"
+
+
 def widen(t, dtype):
     return inputs.widen(host_array(t, dtype), dtype)
 

@@ -6,7 +6,7 @@ import pytest
 import oracle
 from video_audio_diffusion_amd import blk, inputs
 
-from gpu_util import TOL, assert_close, make_device, oracle_inputs, run_block_steps, widen
+from gpu_util import TOL, assert_close, assert_delta_close, make_device, oracle_inputs, run_block_steps, widen
 
 pytestmark = pytest.mark.gpu
 CFG = inputs.CONFIGS[1]
@@ -60,7 +60,7 @@ def test_block_matches_oracle(state):
     x = inputs.widen(host["x"], CFG.dtype)
     got = widen(r["out"], CFG.dtype)
     assert_close("block_out", got, ref["out"], TOL["f32"])
-    assert_close("block_delta", got - x, ref["out"] - x, TOL["f32"])
+    assert_delta_close("block_delta", got, ref["out"], x, TOL["f32"], "f32")
 
 
 def test_attention_lse(state):
