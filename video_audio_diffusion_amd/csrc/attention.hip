@@ -1,12 +1,14 @@
 // Full bidirectional softmax attention, flash style, on MFMA.
 //
-// Work split: one workgroup = 4 wavefronts = 256 query rows of one head;
-// each wavefront owns 64 queries (two 32-query MFMA blocks) for the whole
-// key sweep, so its output accumulators, running max and running sum never
-// leave registers.  Keys stream through LDS in tiles of 64, double-buffered:
-// the next tile is fetched into registers (buffer loads against a per-tile
-// resource, which also zero-fills rows past the last key) while the current
-// tile is multiplied.
+// Work split: one workgroup = 8 wavefronts = 256 query rows of one head;
+// each wavefront owns 32 queries (one 32-query MFMA block) for the whole key
+// sweep, so its output accumulators, running max and running sum never leave
+// registers.  A wavefront needs ~170 VGPRs, so two of them share each SIMD
+// and one's softmax (VALU) runs under the other's MFMAs.  Keys stream
+// through LDS in tiles of 64, double-buffered: the next tile is fetched into
+// registers (buffer loads against a per-tile resource, which also zero-fills
+// rows past the last key) while the current tile is multiplied; wavefronts
+// 0-3 stage (and transpose) V, wavefronts 4-7 stage K.
 //
 // Orientation: the kernel computes S^T = K . Q^T (keys as MFMA rows, queries
 // as MFMA columns).  A 32x32 accumulator then gives each lane one query and
@@ -50,8 +52,9 @@ template <> struct AttnMfma<float> {
     }
 };
 
-constexpr int kAttnWaves = 4;
-constexpr int kQB = 2;                       // 32-query blocks per wavefront
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = kAttnWaves * 64;
+constexpr int kQB = 1;                       // 32-query blocks per wavefront
 constexpr int kBQ = kAttnWaves * kQB * 32;   // 256 queries per workgroup
 constexpr int kBKV = 64;                     // keys per LDS tile
 constexpr int kKB = kBKV / 32;               // 32-key score blocks per tile
@@ -66,7 +69,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ Kp,
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ Kp,
                                                        const T* __restrict__ Vp, int64_t ld,
                                                        T* __restrict__ O, int64_t ldo, int32_t n,
                                                        int32_t heads, float sl2, float* __restrict__ lse,
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
     constexpr int VRBP = kBKV * ES + RUNB;   // padded V^T row (64 keys + one run)
     constexpr int DV = KRB / 16;             // 16-byte vectors per V row
     constexpr int EPV = 16 / ES;             // d values per 16-byte vector
-    constexpr int KSLOTS = kBKV * KCH / 256; // K chunks each thread stages
+    constexpr int KSLOTS = kBKV * KCH / 256; // K chunks each staging thread moves
     constexpr int VPAIRS = 16 * DV;          // (4-key run, d vector) pairs per tile
     constexpr int VSLOTS = (VPAIRS + 255) / 256;
     constexpr int DB = HD / 32;              // 32-wide d blocks of the output
@@ -115,50 +118,68 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
 #pragma unroll
         for (int c = 0; c < NCH; ++c) qf[qb][c] = *reinterpret_cast<const u32x4*>(src + c * 32 + g * 16);
     }
+    // Retire the Q loads here: otherwise the wait-count analysis still sees
+    // them in flight inside the key loop and makes every QK product wait for
+    // the next tile's prefetch as well.
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- K / V staging: K chunk (key tid/KCH + (256/KCH) i, chunk tid%KCH);
-    //      V run (idx % 16) of 4 keys, d vector idx / 16, idx = tid + 256 i
-    const uint32_t k_voff = (uint32_t)(tid / KCH) * ldb + (uint32_t)(tid % KCH) * 16;
-    u32x4 kreg[KSLOTS];
-    u32x4 vreg[VSLOTS][4];
+    // ---- K / V staging.  Threads 0..255 move V: 4-key run (idx % 16) of d
+    //      vector idx / 16, idx = tid + 256 i.  Threads 256..511 move K:
+    //      chunk (st % KCH) of key st / KCH + (256 / KCH) i, st = tid - 256.
+    const bool stage_v = tid < 256;
+    const int st = stage_v ? tid : tid - 256;
+    const uint32_t k_voff = (uint32_t)(st / KCH) * ldb + (uint32_t)(st % KCH) * 16;
+    constexpr int NREG = KSLOTS > 4 * VSLOTS ? KSLOTS : 4 * VSLOTS;
+    u32x4 sreg[NREG];
     auto fetch = [&](int kv0) {
         const int nvalid = n - kv0 < kBKV ? n - kv0 : kBKV;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
+        if (stage_v) {
+            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
 #pragma unroll
-        for (int i = 0; i < KSLOTS; ++i)
-            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff, i * (256 / KCH) * ldb, 0);
+            for (int i = 0; i < VSLOTS; ++i) {
+                const int idx = st + 256 * i;
+                const uint32_t voff = (uint32_t)(4 * (idx % 16)) * ldb + (uint32_t)(idx / 16 % DV) * 16;
 #pragma unroll
-        for (int i = 0; i < VSLOTS; ++i) {
-            const int idx = tid + 256 * i;
-            const uint32_t voff = (uint32_t)(4 * (idx % 16)) * ldb + (uint32_t)(idx / 16 % DV) * 16;
+                for (int e = 0; e < 4; ++e)
+                    sreg[4 * i + e] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, e * ldb, 0);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vreg[i][e] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, e * ldb, 0);
+            for (int i = 0; i < KSLOTS; ++i)
+                sreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff, i * (256 / KCH) * ldb, 0);
+#pragma unroll
+            for (int i = KSLOTS; i < NREG; ++i) sreg[i] = (u32x4){0, 0, 0, 0};   // both paths define every slot
         }
     };
     auto stash = [&](int buf) {
+        if (!stage_v) {
 #pragma unroll
-        for (int i = 0; i < KSLOTS; ++i) {
-            const int key = tid / KCH + (256 / KCH) * i, ch = tid % KCH;
-            *reinterpret_cast<u32x4*>(&ks[buf][key * KRBP + ch * 16]) = kreg[i];
+            for (int i = 0; i < KSLOTS; ++i) {
+                const int key = st / KCH + (256 / KCH) * i, ch = st % KCH;
+                *reinterpret_cast<u32x4*>(&ks[buf][key * KRBP + ch * 16]) = sreg[i];
+            }
+            return;
         }
 #pragma unroll
         for (int i = 0; i < VSLOTS; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx >= VPAIRS) break;
-            const int run = idx % 16, dv = idx / 16;
+            const int idx = st + 256 * i;
+            if (VPAIRS % 256 == 0 || idx < VPAIRS) {
+                const int run = idx % 16, dv = idx / 16;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                char* dst = &vts[buf][(dv * EPV + e) * VRBP + run * RUNB];
-                if constexpr (ES == 2) {
-                    // element e of each of the 4 keys' 8 bf16
-                    uint32_t w[4];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) w[kk] = (vreg[i][kk][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                    *reinterpret_cast<u32x2*>(dst) = (u32x2){w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-                } else {
-                    *reinterpret_cast<u32x4*>(dst) =
-                        (u32x4){vreg[i][0][e], vreg[i][1][e], vreg[i][2][e], vreg[i][3][e]};
+                for (int e = 0; e < EPV; ++e) {
+                    char* dst = &vts[buf][(dv * EPV + e) * VRBP + run * RUNB];
+                    if constexpr (ES == 2) {
+                        // d = 2w (+1): low (high) bf16 of dword w of each key's vector
+                        const int w = e >> 1;
+                        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                        *reinterpret_cast<u32x2*>(dst) =
+                            (u32x2){__builtin_amdgcn_perm(sreg[4 * i + 1][w], sreg[4 * i][w], sel),
+                                    __builtin_amdgcn_perm(sreg[4 * i + 3][w], sreg[4 * i + 2][w], sel)};
+                    } else {
+                        *reinterpret_cast<u32x4*>(dst) =
+                            (u32x4){sreg[4 * i][e], sreg[4 * i + 1][e], sreg[4 * i + 2][e], sreg[4 * i + 3][e]};
+                    }
                 }
             }
         }
@@ -331,7 +352,7 @@ hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v
     const int grid = nqt * heads;
     const float sl2 = (float)((double)scale * 1.4426950408889634);
 #define H3_ATTN(TY, D)                                                                                  \
-    attn_fwd_kernel<TY, D><<<grid, 256, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld, (TY*)o, \
+    attn_fwd_kernel<TY, D><<<grid, kAttnThreads, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld, (TY*)o, \
                                                  ldo, n, heads, sl2, lse, nqt)
     if (bf) {
         if (hd == 128) H3_ATTN(bf16, 128);
