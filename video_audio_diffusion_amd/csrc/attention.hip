@@ -3,33 +3,44 @@
 // Work split: one workgroup = 8 wavefronts = 256 query rows of one head;
 // each wavefront owns 32 queries (one 32-query MFMA block) for the whole key
 // sweep, so its output accumulators, running max and running sum never leave
-// registers.  A wavefront needs ~170 VGPRs, so two of them share each SIMD
-// and one's softmax (VALU) runs under the other's MFMAs.  Keys stream
-// through LDS in tiles of 64, double-buffered: the next tile is fetched into
-// registers (buffer loads against a per-tile resource, which also zero-fills
-// rows past the last key) while the current tile is multiplied; wavefronts
-// 0-3 stage (and transpose) V, wavefronts 4-7 stage K.
+// registers.  Two wavefronts share each SIMD, so one's softmax (VALU) can run
+// under the other's MFMAs.
+//
+// Key/value tiles (128 keys for 16-bit data) are copied from global memory
+// straight into LDS by buffer->LDS loads, double-buffered in two LDS objects:
+// the copy of tile t+1 runs while tile t is multiplied.  The buffer
+// resource of each tile stops at the last key, so rows past the end arrive
+// as zeros.  Rows are stored in LDS as they are in memory ([key][d]) with
+// their 16-byte chunks XOR-permuted per row, which keeps both fragment reads
+// below free of bank conflicts.
 //
 // Orientation: the kernel computes S^T = K . Q^T (keys as MFMA rows, queries
 // as MFMA columns).  A 32x32 accumulator then gives each lane one query and
-// 16 keys, so a query's block max is 15 local max operations plus one swap
-// with lane^32, and the probabilities P^T are already in the B-operand
-// layout of the second product O^T += V^T . P^T -- no LDS round trip for P.
-// Accumulator register r of lane l holds key 8(r/4) + 4(l/32) + r%4 of its
-// 32-key block.  The PV product contracts over keys in that same order, so
-// V^T is read from LDS as runs of 4 consecutive keys at key offsets
-// 8(r/4) + 4(l/32): V is stored transposed ([d][key]) in LDS.
-//
-// LDS rows are padded (K rows by 16 bytes, V^T rows by one 4-key run) so
-// that the 32 rows one fragment read touches fall on distinct banks while
-// every address stays base + constant.
+// 16 keys -- register r of lane l holds key 8(r/4) + 4(l/32) + r%4 of its
+// 32-key block -- so a query's block max is local max operations plus one
+// swap with lane^32, and the probabilities P^T are already in the B-operand
+// layout of the second product O^T += V^T . P^T.  The A operand V^T comes
+// from row-major V through the LDS transpose read (ds_read_b64_tr_b16): in
+// each 16-lane group every lane reads 4 consecutive 16-bit values and lane
+// 4a + e receives value e of lanes a, 4 + a, 8 + a and 12 + a.  Lane
+// 16q + 4r + a reads key 4(q/2) + r of a 16-key half-block at d offset
+// 16(q%2) + 4a, so lane l receives V[key][d = l % 32] for the four keys
+// 4(l/32) + 0..3 -- the same keys, in the same order, as its P^T register
+// run.  (For fp32 the MFMA takes one key per lane; V^T is read element-wise.)
 //
 // Softmax: logits are scaled by scale*log2(e) once; exponentials are exp2
 // (v_exp_f32).  Each query keeps a reference max m and a running sum l per
-// lane; the two lane halves of a query are summed once at the end.
+// lane; the two lane halves of a query are summed once at the end.  Within a
+// tile the QK product of the next 32-key block is issued in the same basic
+// block as the softmax of the current one, so the MFMA pipe has independent
+// work while the exponentials run.
 #include "launch.h"
 
 namespace h3 {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define H3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define H3_LDS_S4(p) ((__attribute__((address_space(3))) s16x4*)(p))
 
 template <typename T> struct AttnMfma;
 
@@ -54,44 +65,59 @@ template <> struct AttnMfma<float> {
 
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = kAttnWaves * 64;
-constexpr int kQB = 1;                       // 32-query blocks per wavefront
-constexpr int kBQ = kAttnWaves * kQB * 32;   // 256 queries per workgroup
-constexpr int kBKV = 64;                     // keys per LDS tile
-constexpr int kKB = kBKV / 32;               // 32-key score blocks per tile
+constexpr int kBQ = kAttnWaves * 32;         // 256 queries per workgroup
 // The reference max of a query only moves when a block's max exceeds it by
 // more than this (log2 units), so probabilities stay <= 2^8 and the output
 // rescale is skipped for most blocks; the result is unchanged because the
 // final division uses the same reference.
 constexpr float kLazyMax = 8.0f;
 
+// 16-byte chunk c of the row of key `key` sits at chunk c ^ swz(key).
+template <int CH> __device__ __forceinline__ int kswz(int key) { return key & (CH >= 16 ? 15 : CH - 1); }
+template <int CH> __device__ __forceinline__ int vswz(int key) {
+    return CH >= 16 ? (key & 3) << 2 : (key & 2) << 1;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <typename T, int HD>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ Kp,
-                                                       const T* __restrict__ Vp, int64_t ld,
-                                                       T* __restrict__ O, int64_t ldo, int32_t n,
-                                                       int32_t heads, float sl2, float* __restrict__ lse,
-                                                       int32_t nqt) {
-    constexpr int ES = sizeof(T);
-    constexpr int KRB = HD * ES;             // bytes of one K row
-    constexpr int KRBP = KRB + 16;           // padded K row in LDS
-    constexpr int KCH = KRB / 16;            // 16-byte chunks per K row
-    constexpr int NCH = KRB / 32;            // 32-byte MFMA k-chunks over head_dim
-    constexpr int RUNB = 4 * ES;             // bytes of a 4-key run of V^T
-    constexpr int VRBP = kBKV * ES + RUNB;   // padded V^T row (64 keys + one run)
-    constexpr int DV = KRB / 16;             // 16-byte vectors per V row
-    constexpr int EPV = 16 / ES;             // d values per 16-byte vector
-    constexpr int KSLOTS = kBKV * KCH / 256; // K chunks each staging thread moves
-    constexpr int VPAIRS = 16 * DV;          // (4-key run, d vector) pairs per tile
-    constexpr int VSLOTS = (VPAIRS + 255) / 256;
-    constexpr int DB = HD / 32;              // 32-wide d blocks of the output
-    static_assert(KSLOTS >= 1 && (kBKV * KCH) % 256 == 0 && 256 % KCH == 0, "K tile split");
-    static_assert(VPAIRS <= 256 || VPAIRS % 256 == 0, "V tile split");
+// Copy one K tile and one V tile into LDS (K at buf, V at buf + TILE): the
+// wavefront's IPW 1 KB pieces of each, lane offsets precomputed in dk / dv.
+template <int IPW, int TILE, typename T>
+__device__ __forceinline__ void copy_kv_tile(char* buf, int wave, const T* Kp, const T* Vp, int64_t hoff, int kv0,
+                                             int n, int bkv, int64_t ld, uint32_t ldb, const uint32_t* dk,
+                                             const uint32_t* dv) {
+    const int nvalid = n - kv0 < bkv ? n - kv0 : bkv;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, H3_LDS(buf + (wave * IPW + i) * 1024), 16, dk[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(buf + TILE + (wave * IPW + i) * 1024), 16, dv[i], 0, 0,
+                                                 0);
+}
 
-    __shared__ __attribute__((aligned(16))) char ks[2][kBKV * KRBP];
-    __shared__ __attribute__((aligned(16))) char vts[2][HD * VRBP];
+template <typename T, int HD>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ Kp, const T* __restrict__ Vp, int64_t ld,
+    T* __restrict__ O, int64_t ldo, int32_t n, int32_t heads, float sl2, float* __restrict__ lse,
+    int32_t nqt) {
+    constexpr int ES = sizeof(T);
+    constexpr int RB = HD * ES;                  // bytes of one K or V row
+    constexpr int CH = RB / 16;                  // 16-byte chunks per row
+    constexpr int BKV = RB <= 256 ? 128 : 64;    // keys per tile
+    constexpr int NKB = BKV / 32;                // 32-key blocks per tile
+    constexpr int TILE = BKV * RB;               // bytes of one operand tile
+    constexpr int IPW = TILE / (1024 * kAttnWaves);   // 1 KB copies per wavefront per operand
+    constexpr int NCH = RB / 32;                 // 32-byte MFMA k-chunks over head_dim
+    constexpr int DB = HD / 32;                  // 32-wide d blocks of the output
+    static_assert(IPW >= 1 && TILE % (1024 * kAttnWaves) == 0, "tile split");
+
+    __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];   // [K tile | V tile]
+    __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];
 
     // ---- workgroup -> (head, query tile); consecutive tiles on one XCD share a head
     const int G = heads * nqt;
@@ -103,245 +129,201 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(const T* __re
     const int qt = L - head * nqt;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, g = lane >> 5;
-    const int q0 = qt * kBQ + wave * (kQB * 32);
+    const int q0 = qt * kBQ + wave * 32;
     const int64_t hoff = (int64_t)head * HD;
-    const uint32_t ldb = (uint32_t)(ld * ES);   // bytes between key rows
+    const uint32_t ldb = (uint32_t)(ld * ES);    // bytes between key rows
 
     // ---- Q^T fragments (B operand): lane holds one query, 16 bytes of d per chunk
-    u32x4 qf[kQB][NCH];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = q0 + qb * 32 + col;
+    u32x4 qf[NCH];
+    {
+        const int qi = q0 + col;
         const char* src = reinterpret_cast<const char*>(Q + (int64_t)(qi < n ? qi : n - 1) * ld + hoff);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) qf[qb][c] = *reinterpret_cast<const u32x4*>(src + c * 32 + g * 16);
-    }
-    // Retire the Q loads here: otherwise the wait-count analysis still sees
-    // them in flight inside the key loop and makes every QK product wait for
-    // the next tile's prefetch as well.
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // ---- K / V staging.  Threads 0..255 move V: 4-key run (idx % 16) of d
-    //      vector idx / 16, idx = tid + 256 i.  Threads 256..511 move K:
-    //      chunk (st % KCH) of key st / KCH + (256 / KCH) i, st = tid - 256.
-    const bool stage_v = tid < 256;
-    const int st = stage_v ? tid : tid - 256;
-    const uint32_t k_voff = (uint32_t)(st / KCH) * ldb + (uint32_t)(st % KCH) * 16;
-    constexpr int NREG = KSLOTS > 4 * VSLOTS ? KSLOTS : 4 * VSLOTS;
-    u32x4 sreg[NREG];
-    auto fetch = [&](int kv0) {
-        const int nvalid = n - kv0 < kBKV ? n - kv0 : kBKV;
-        if (stage_v) {
-            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
-#pragma unroll
-            for (int i = 0; i < VSLOTS; ++i) {
-                const int idx = st + 256 * i;
-                const uint32_t voff = (uint32_t)(4 * (idx % 16)) * ldb + (uint32_t)(idx / 16 % DV) * 16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sreg[4 * i + e] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, e * ldb, 0);
-            }
-        } else {
-            const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
-#pragma unroll
-            for (int i = 0; i < KSLOTS; ++i)
-                sreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff, i * (256 / KCH) * ldb, 0);
-#pragma unroll
-            for (int i = KSLOTS; i < NREG; ++i) sreg[i] = (u32x4){0, 0, 0, 0};   // both paths define every slot
-        }
-    };
-    auto stash = [&](int buf) {
-        if (!stage_v) {
-#pragma unroll
-            for (int i = 0; i < KSLOTS; ++i) {
-                const int key = st / KCH + (256 / KCH) * i, ch = st % KCH;
-                *reinterpret_cast<u32x4*>(&ks[buf][key * KRBP + ch * 16]) = sreg[i];
-            }
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < VSLOTS; ++i) {
-            const int idx = st + 256 * i;
-            if (VPAIRS % 256 == 0 || idx < VPAIRS) {
-                const int run = idx % 16, dv = idx / 16;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    char* dst = &vts[buf][(dv * EPV + e) * VRBP + run * RUNB];
-                    if constexpr (ES == 2) {
-                        // d = 2w (+1): low (high) bf16 of dword w of each key's vector
-                        const int w = e >> 1;
-                        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                        *reinterpret_cast<u32x2*>(dst) =
-                            (u32x2){__builtin_amdgcn_perm(sreg[4 * i + 1][w], sreg[4 * i][w], sel),
-                                    __builtin_amdgcn_perm(sreg[4 * i + 3][w], sreg[4 * i + 2][w], sel)};
-                    } else {
-                        *reinterpret_cast<u32x4*>(dst) =
-                            (u32x4){sreg[4 * i][e], sreg[4 * i + 1][e], sreg[4 * i + 2][e], sreg[4 * i + 3][e]};
-                    }
-                }
-            }
-        }
-    };
-
-    f32x16 oacc[kQB][DB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] = (f32x16){};
-    float m_run[kQB], l_run[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        m_run[qb] = -__builtin_inff();
-        l_run[qb] = 0.f;
+        for (int c = 0; c < NCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(src + c * 32 + g * 16);
     }
 
-    const int ntiles = (n + kBKV - 1) / kBKV;
-    fetch(0);
-    stash(0);
-    __syncthreads();
+    // ---- tile copies: LDS chunk p = 64 (wave IPW + i) + lane of a tile is
+    //      chunk (p % CH) ^ swz(key) of key p / CH
+    uint32_t dk[IPW], dv[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = 64 * (wave * IPW + i) + lane;
+        const int key = p / CH, ph = p % CH;
+        dk[i] = (uint32_t)key * ldb + (uint32_t)((ph ^ kswz<CH>(key)) << 4);
+        dv[i] = (uint32_t)key * ldb + (uint32_t)((ph ^ vswz<CH>(key)) << 4);
+    }
+    // ---- fragment read offsets (constant per lane)
+    // K chunk (2c + g) of key kb*32 + col
+    uint32_t ko[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) ko[c] = (uint32_t)(col * RB + (((2 * c + g) ^ kswz<CH>(col)) << 4));
+    // V transpose read: lane 16q + 4r + a reads key 4(q/2) + r of a 16-key
+    // half-block and d = 32 db + 16(q%2) + 4a .. +3
+    uint32_t vo[DB];
+    {
+        const int q = lane >> 4, r = (lane >> 2) & 3, a = lane & 3;
+        const int kr = 4 * (q >> 1) + r;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int c = 4 * db + 2 * (q & 1) + (a >> 1);
+            vo[db] = (uint32_t)(kr * RB + ((c ^ vswz<CH>(kr)) << 4) + (a & 1) * 8);
+        }
+    }
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int kv0 = t * kBKV;
-        if (t + 1 < ntiles) fetch(kv0 + kBKV);
-        const char* K_l = ks[buf] + col * KRBP + g * 16;
-        const char* V_l = vts[buf] + col * VRBP + g * RUNB;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+    float m_run = -__builtin_inff(), l_run = 0.f;
 
+    auto qk_block = [&](f32x16& s, const u32x4* kf) {
+        s = (f32x16){};
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-            if (kv0 + kb * 32 >= n) break;          // block entirely past the last key
-            // ---- S^T = K Q^T for 32 keys x (kQB x 32) queries
-            f32x16 s[kQB];
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[qb] = (f32x16){};
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(K_l + kb * 32 * KRBP + c * 32);
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) AttnMfma<T>::qk(s[qb], kf, qf[qb][c]);
-            }
-            if (kv0 + kb * 32 + 32 > n) {           // ragged block: keys past n get -inf
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= n)
-#pragma unroll
-                        for (int qb = 0; qb < kQB; ++qb) s[qb][r] = -__builtin_inff();
-                }
-            }
+        for (int c = 0; c < NCH; ++c) AttnMfma<T>::qk(s, kf[c], qf[c]);
+    };
 
-            // ---- online softmax with a lazily moved reference max
-            float mx[kQB];
-            bool grow = false;
+    auto tile = [&](const char* buf, int kv0) {
+        const char* KB = buf;
+        const char* VB = buf + TILE;
+        u32x4 kf[NCH];
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                float v = s[qb][0];
+        for (int c = 0; c < NCH; ++c) kf[c] = *reinterpret_cast<const u32x4*>(KB + ko[c]);
+        f32x16 s;
+        qk_block(s, kf);
 #pragma unroll
-                for (int r = 1; r < 16; ++r) v = fmaxf(v, s[qb][r]);
-                v = fmaxf(v, __shfl_xor(v, 32, kWave)) * sl2;
-                mx[qb] = v;
-                grow |= v > m_run[qb] + kLazyMax;
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int kbase = kv0 + kb * 32;
+            if (kbase >= n) break;                        // block entirely past the last key
+            if (kbase + 32 > n) {                         // ragged block: keys past n get -inf
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kbase + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s[r] = -__builtin_inff();
             }
-            if (__builtin_amdgcn_ballot_w64(grow)) {   // some query's max moved by > 2^kLazyMax
+            // K fragments of the next block (its QK runs under this block's softmax)
+            if (kb + 1 < NKB) {
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) {
-                    const float m_new = fmaxf(m_run[qb], mx[qb]);
-                    const float alpha = fast_exp2(m_run[qb] - m_new);
-                    m_run[qb] = m_new;
-                    l_run[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-                }
+                for (int c = 0; c < NCH; ++c)
+                    kf[c] = *reinterpret_cast<const u32x4*>(KB + (kb + 1) * 32 * RB + ko[c]);
             }
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                float rs = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(s[qb][r], sl2, -m_run[qb]));
-                    s[qb][r] = p;
-                    rs += p;
-                }
-                l_run[qb] += rs;
-            }
-
-            // ---- O^T += V^T P^T over these 32 keys
+            // V^T fragments of this block
+            u32x4 vf[DB][2];
             if constexpr (ES == 2) {
-                // one MFMA per 16 keys: P regs 8h..8h+7; V^T runs at keys 16h + 4g and 16h + 8 + 4g
-                u32x4 pf[kQB][2];
 #pragma unroll
-                for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            pf[qb][h][w] = pack_bf16x2(s[qb][8 * h + 2 * w], s[qb][8 * h + 2 * w + 1]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const char* vp = V_l + db * 32 * VRBP + (kb * 32 + 16 * h) * ES;
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8 * ES);
-                        const u32x4 vf = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                        for (int qb = 0; qb < kQB; ++qb)
-                            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[qb][h]),
-                                oacc[qb][db], 0, 0, 0);
+                        const char* vp = VB + (kb * 32 + 16 * h) * RB + vo[db];
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp + 8 * RB));
+                        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                        vf[db][h] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
                     }
-                }
+            }
+
+            // ---- softmax of this block: block max, lazily moved reference
+            float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+            for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
+            const bool grow = mx > m_run + kLazyMax;
+            const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            float rs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_new));
+                rs += s[r];
+            }
+            l_run = __builtin_fmaf(l_run, alpha, rs);
+
+            // ---- QK of the next block (independent MFMA work)
+            f32x16 s_next;
+            if (kb + 1 < NKB) qk_block(s_next, kf);
+
+            if (__builtin_amdgcn_ballot_w64(grow)) {      // rare: some reference moved
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            }
+
+            // ---- O^T += V^T P^T over this block
+            if constexpr (ES == 2) {
+                u32x4 pf[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) pf[h][w] = pack_bf16x2(s[8 * h + 2 * w], s[8 * h + 2 * w + 1]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, vf[db][h]), __builtin_bit_cast(bf16x8, pf[h]), oacc[db], 0,
+                            0, 0);
             } else {
-                // fp32: four 32x32x2 MFMAs per 8 keys; lane group g holds keys 8c + 4g .. +3
+                // fp32: four 32x32x2 MFMAs per 8 keys; MFMA j of group c takes key 8c + 4g + j
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
+                    const int d = db * 32 + col;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const f32x4 vf = *reinterpret_cast<const f32x4*>(V_l + db * 32 * VRBP +
-                                                                         (kb * 32 + 8 * c) * ES);
+                    for (int c = 0; c < 4; ++c)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-#pragma unroll
-                            for (int qb = 0; qb < kQB; ++qb)
-                                oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[j], s[qb][4 * c + j],
-                                                                                   oacc[qb][db], 0, 0, 0);
-                    }
+                        for (int j = 0; j < 4; ++j) {
+                            const int key = kb * 32 + 8 * c + 4 * g + j;
+                            const float v = *reinterpret_cast<const float*>(
+                                VB + key * RB + (((d >> 2) ^ vswz<CH>(key)) << 4) + (d & 3) * 4);
+                            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, s[4 * c + j], oacc[db], 0, 0, 0);
+                        }
                 }
             }
+            if (kb + 1 < NKB) s = s_next;
         }
+    };
 
-        if (t + 1 < ntiles) stash(buf ^ 1);
+    // Retire the Q loads before the key loop: otherwise the wait-count
+    // analysis still sees them in flight there and makes the QK products
+    // wait for tile copies as well.
+    __builtin_amdgcn_s_waitcnt(0);
+    const int ntiles = (n + BKV - 1) / BKV;
+    copy_kv_tile<IPW, TILE>(lds0, wave, Kp, Vp, hoff, 0, n, BKV, ld, ldb, dk, dv);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) copy_kv_tile<IPW, TILE>(lds1, wave, Kp, Vp, hoff, (t + 1) * BKV, n, BKV, ld, ldb, dk, dv);
+        tile(lds0, t * BKV);
+        __builtin_amdgcn_s_waitcnt(0);    // this wave's copies into lds1 have landed
+        __syncthreads();                  // ... everyone's, and lds0 is free again
+        if (t + 1 >= ntiles) break;
+        if (t + 2 < ntiles) copy_kv_tile<IPW, TILE>(lds0, wave, Kp, Vp, hoff, (t + 2) * BKV, n, BKV, ld, ldb, dk, dv);
+        tile(lds1, (t + 1) * BKV);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     // ---- normalise and store: O^T lane (query, g) holds d = 32db + 8(r/4) + 4g + r%4
+    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    const float inv = 1.0f / l_tot;
+    const int qi = q0 + col;
+    if (qi < n) {
+        T* orow = O + (int64_t)qi * ldo + hoff;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, kWave);
-        const float inv = 1.0f / l_tot;
-        const int qi = q0 + qb * 32 + col;
-        if (qi < n) {
-            T* orow = O + (int64_t)qi * ldo + hoff;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = db * 32 + 8 * r4 + 4 * g;
-                    const f32x16& a = oacc[qb][db];
-                    if constexpr (ES == 2) {
-                        *reinterpret_cast<u32x2*>(orow + d) =
-                            (u32x2){pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
-                                    pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
-                    } else {
-                        *reinterpret_cast<f32x4*>(orow + d) =
-                            (f32x4){a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv};
-                    }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                const f32x16& a = oacc[db];
+                if constexpr (ES == 2) {
+                    *reinterpret_cast<u32x2*>(orow + d) =
+                        (u32x2){pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
+                                pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
+                } else {
+                    *reinterpret_cast<f32x4*>(orow + d) =
+                        (f32x4){a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv};
                 }
-            if (lse && g == 0)
-                lse[(int64_t)head * n + qi] = m_run[qb] * 0.69314718055994531f + __logf(l_tot);
-        }
+            }
+        if (lse && g == 0) lse[(int64_t)head * n + qi] = m_run * 0.69314718055994531f + __logf(l_tot);
     }
 }
 
@@ -351,9 +333,9 @@ hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v
     const int nqt = (n + kBQ - 1) / kBQ;
     const int grid = nqt * heads;
     const float sl2 = (float)((double)scale * 1.4426950408889634);
-#define H3_ATTN(TY, D)                                                                                  \
-    attn_fwd_kernel<TY, D><<<grid, kAttnThreads, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld, (TY*)o, \
-                                                 ldo, n, heads, sl2, lse, nqt)
+#define H3_ATTN(TY, D)                                                                                    \
+    attn_fwd_kernel<TY, D><<<grid, kAttnThreads, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld,  \
+                                                          (TY*)o, ldo, n, heads, sl2, lse, nqt)
     if (bf) {
         if (hd == 128) H3_ATTN(bf16, 128);
         else H3_ATTN(bf16, 64);
