@@ -39,7 +39,6 @@
 namespace h3 {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define H3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define H3_LDS_S4(p) ((__attribute__((address_space(3))) s16x4*)(p))
 
 template <typename T> struct AttnMfma;
@@ -76,10 +75,6 @@ constexpr float kLazyMax = 8.0f;
 template <int CH> __device__ __forceinline__ int kswz(int key) { return key & (CH >= 16 ? 15 : CH - 1); }
 template <int CH> __device__ __forceinline__ int vswz(int key) {
     return CH >= 16 ? (key & 3) << 2 : (key & 2) << 1;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Copy one K tile and one V tile into LDS (K at buf, V at buf + TILE): the

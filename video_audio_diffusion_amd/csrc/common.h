@@ -92,4 +92,13 @@ __device__ __forceinline__ float sum_lanes(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes): loads at or past `bytes`
+// return zeros, which is how tiles that run past the last row are padded.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+#define H3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 }  // namespace h3
