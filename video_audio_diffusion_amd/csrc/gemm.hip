@@ -7,18 +7,18 @@
 // 16-byte vectors.
 //
 // Tile: 256 x 256 per workgroup, 4 wavefronts in a 2 x 2 layout, 128 x 128
-// (4 x 4 MFMA blocks, 256 accumulator registers) per wavefront; 128 bytes of
-// K per step (64 bf16 or 32 fp32).  Each step's A and W tiles are copied from
-// global memory straight into LDS by buffer->LDS loads into one of two LDS
-// buffer pairs, so the copy of step k+1 runs while step k is multiplied; the
-// buffer resources stop at row M (N), so tiles that run past the end are
-// padded with zeros.  Inside a step all fragments are read from LDS before
-// the step's 64 MFMAs are issued.
+// (4 x 4 MFMA blocks, 256 accumulator registers) per wavefront; 64 bytes of
+// K per step (32 bf16 or 16 fp32).  Each step's A and W tiles are copied from
+// global memory straight into LDS by buffer->LDS loads into a 4-stage ring
+// (128 KB), so the copies of the next three steps are in flight while a
+// step is multiplied; the buffer resources stop at row M (N), so tiles that
+// run past the end are padded with zeros.  Fragments are double-buffered in
+// registers per 32-byte k-chunk: the reads of the next chunk are issued
+// before the current chunk's 16 MFMAs, so LDS latency hides under them.
 //
-// LDS rows are XOR-swizzled in 16-byte chunks: chunk c of row r lives at
-// c ^ ((r >> 1) & 7), so any 16 consecutive rows read at one chunk -- a
-// fragment read -- and any two rows written whole land on 16 distinct
-// 16-byte slots of the 256-byte bank window.
+// LDS rows (64 bytes) are XOR-swizzled in 16-byte chunks: chunk c of row r
+// lives at c ^ ((r >> 2) & 3), so the 16 rows of a half-wavefront fragment
+// read land on 16 distinct 16-byte slots of the 256-byte bank window.
 //
 // Tiles are numbered so that consecutive workgroups on one XCD (hardware
 // deals workgroups to the 8 XCDs round-robin) form GROUP_M x n blocks of the
@@ -50,18 +50,31 @@ template <> struct GemmMfma<float> {
     __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
 };
 
-constexpr int kBM = 256, kBN = 256, kRowBytes = 128, kGroupM = 8;
-constexpr int kTileBytes = kBM * kRowBytes;   // 32 KB per operand per stage
+constexpr int kBM = 256, kBN = 256, kGroupM = 8;
+constexpr int kRowBytes = 64;                  // bytes of K per step and tile row
+constexpr int kStages = 4;                     // LDS ring depth: 3 steps of lookahead
+constexpr int kTileBytes = kBM * kRowBytes;    // 16 KB per operand per stage
+constexpr int kPieces = kTileBytes / 1024 / 4; // 1 KB copies per wavefront per operand
+
+// s_waitcnt immediate: at most n vector-memory operations of this wavefront
+// outstanding and, with lgkm0, no LDS operation outstanding (the expcnt
+// field is left unconstrained).
+template <int n, bool lgkm0>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((((n >> 4) & 3) << 14) | ((lgkm0 ? 0 : 0xF) << 8) | (0x7 << 4) | (n & 15));
+}
 
 // Copy this wavefront's quarter (64 rows) of one operand's k-step tile into
-// LDS: 8 pieces of 1 KB (8 rows each); lane offsets precomputed in voff,
-// koff = byte offset of the k-step inside a row.
+// LDS: kPieces pieces of 1 KB (16 rows each); lane offsets precomputed in
+// voff, koff = byte offset of the k-step inside a row.
 __device__ __forceinline__ void copy_operand(char* lds, int wave, const void* base, uint32_t bytes,
                                              const uint32_t* voff, uint32_t koff) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base, bytes);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(lds + (wave * 8 + j) * 1024), 16, voff[j], koff, 0, 0);
+    for (int j = 0; j < kPieces; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(lds + (wave * kPieces + j) * 1024), 16, voff[j], koff, 0,
+                                                 0);
 }
 
 template <typename T>
@@ -71,10 +84,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
                                                    int32_t K, int32_t tiles_m, int32_t tiles_n) {
     constexpr int ES = sizeof(T);
     constexpr int BK = kRowBytes / ES;                  // elements of K per step
-    __shared__ __attribute__((aligned(1024))) char sa0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sw0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sa1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sw1[kTileBytes];
+    constexpr int KCH = kRowBytes / 32;                 // 32-byte MFMA k-chunks per step
+    // stage s: A tile at ring + 2 s kTileBytes, W tile right after it
+    __shared__ __attribute__((aligned(1024))) char ring[kStages * 2 * kTileBytes];
 
     // ---- tile order: XCD-contiguous, then GROUP_M-grouped
     const int G = tiles_m * tiles_n;
@@ -96,14 +108,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
     const int wm = wave >> 1, wn = wave & 1;
 
     // ---- copy offsets: piece j of this wavefront holds tile rows
-    //      64 wave + 8 j + lane / 8; LDS slot lane % 8 of the row gets chunk
-    //      (lane % 8) ^ ((row >> 1) & 7)
+    //      64 wave + 16 j + lane / 4; LDS slot lane % 4 of the row gets chunk
+    //      (lane % 4) ^ ((row >> 2) & 3)
     const uint32_t ldab = (uint32_t)(lda * ES), ldwb = (uint32_t)(ldw * ES);
-    uint32_t va[8], vw[8];
+    uint32_t va[kPieces], vw[kPieces];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = 64 * wave + 8 * j + (lane >> 3);
-        const uint32_t c = (uint32_t)((lane & 7) ^ ((row >> 1) & 7));
+    for (int j = 0; j < kPieces; ++j) {
+        const int row = 64 * wave + 16 * j + (lane >> 2);
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
         va[j] = (uint32_t)row * ldab + c * 16;
         vw[j] = (uint32_t)row * ldwb + c * 16;
     }
@@ -111,14 +123,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
     const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
     const T* a_base = A + (int64_t)m0 * lda;
     const T* w_base = W + (int64_t)n0 * ldw;
+    auto copy_step = [&](int ks) {
+        char* st = ring + (ks % kStages) * 2 * kTileBytes;
+        copy_operand(st, wave, a_base, bytes_a, va, (uint32_t)ks * kRowBytes);
+        copy_operand(st + kTileBytes, wave, w_base, bytes_w, vw, (uint32_t)ks * kRowBytes);
+    };
 
     // ---- fragment offsets: row (32 i + frow) of the wave's 128-row panel,
-    //      chunk 2 kk + fhalf; (row >> 1) & 7 depends on frow only
+    //      chunk 2 kk + fhalf; (row >> 2) & 3 depends on frow only
     const int frow = lane & 31, fhalf = lane >> 5;
-    uint32_t fo[4];
+    uint32_t fo[KCH];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) fo[kk] = (uint32_t)(frow * kRowBytes + (((2 * kk + fhalf) ^ ((frow >> 1) & 7)) << 4));
-    const int a_panel = wm * 128 * kRowBytes, w_panel = wn * 128 * kRowBytes;
+    for (int kk = 0; kk < KCH; ++kk)
+        fo[kk] = (uint32_t)(frow * kRowBytes + (((2 * kk + fhalf) ^ ((frow >> 2) & 3)) << 4));
+    const int a_panel = wm * 128 * kRowBytes, w_panel = kTileBytes + wn * 128 * kRowBytes;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -126,43 +144,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-    // One k-step from LDS: all 32 fragment reads first (LDS returns them in
-    // order, so the MFMAs of chunk kk only wait for chunk kk's reads), then
-    // 4 k-chunks x 16 MFMAs.
-    auto compute = [&](const char* As, const char* Ws) {
-        u32x4 af[4][4], bw[4][4];
+    // Fragments are double-buffered per 32-byte k-chunk: slot kk holds chunk
+    // kk of a step (4 A + 4 W 16-byte reads), and the next chunk's reads are
+    // issued before the current chunk's 16 MFMAs.
+    static_assert(KCH == 2, "one register slot per k-chunk of a step");
+    u32x4 fa[KCH][4], fw[KCH][4];
+    auto read_chunk = [&](int ks, int kk, u32x4 (&a)[4], u32x4 (&w)[4]) {
+        const char* st = ring + (ks % kStages) * 2 * kTileBytes;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int i = 0; i < 4; ++i) {
+            a[i] = *reinterpret_cast<const u32x4*>(st + a_panel + i * 32 * kRowBytes + fo[kk]);
+            w[i] = *reinterpret_cast<const u32x4*>(st + w_panel + i * 32 * kRowBytes + fo[kk]);
+        }
+    };
+    auto mfma_chunk = [&](const u32x4 (&a)[4], const u32x4 (&w)[4]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[kk][i] = *reinterpret_cast<const u32x4*>(As + a_panel + i * 32 * kRowBytes + fo[kk]);
-                bw[kk][i] = *reinterpret_cast<const u32x4*>(Ws + w_panel + i * 32 * kRowBytes + fo[kk]);
-            }
-        __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) GemmMfma<T>::mma(acc[i][j], af[kk][i], bw[kk][j]);
+            for (int j = 0; j < 4; ++j) GemmMfma<T>::mma(acc[i][j], a[i], w[j]);
+    };
+    // Wait until step s has landed in LDS for every wavefront and this
+    // wavefront's reads of the step before are done: at most the copies of
+    // steps s+1, s+2 (already issued) may still be outstanding.  Then the
+    // stage of step s-1 is free for the copy of step s+3.  A plain s_barrier
+    // is used: __syncthreads() would also wait for the later copies.
+    auto step_ready = [&](int s, int nk) {
+        if (s + 2 < nk) wait_vm<4 * kPieces, true>();
+        else if (s + 1 < nk) wait_vm<2 * kPieces, true>();
+        else wait_vm<0, true>();
+        __builtin_amdgcn_s_barrier();
+        if (s + kStages - 1 < nk) copy_step(s + kStages - 1);
     };
 
     const int nk = K / BK;
-    copy_operand(sa0, wave, a_base, bytes_a, va, 0);
-    copy_operand(sw0, wave, w_base, bytes_w, vw, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) copy_step(s);
+    step_ready(0, nk);
+    read_chunk(0, 0, fa[0], fw[0]);
     for (int ks = 0; ks < nk; ++ks) {
-        // buffer pair ks & 1 holds this step; the copy of step ks + 1 goes to the other
-        const bool odd = ks & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        // Chunk 0's reads were issued a whole chunk of MFMAs ago; retiring
+        // them here keeps at most 8 LDS reads in flight (the counter holds 15).
+        wait_vm<63, true>();
+        read_chunk(ks, 1, fa[1], fw[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(fa[0], fw[0]);
+        __builtin_amdgcn_sched_barrier(0);
         if (ks + 1 < nk) {
-            copy_operand(odd ? sa0 : sa1, wave, a_base, bytes_a, va, (uint32_t)(ks + 1) * kRowBytes);
-            copy_operand(odd ? sw0 : sw1, wave, w_base, bytes_w, vw, (uint32_t)(ks + 1) * kRowBytes);
+            step_ready(ks + 1, nk);
+            read_chunk(ks + 1, 0, fa[0], fw[0]);
         }
-        compute(odd ? sa1 : sa0, odd ? sw1 : sw0);
-        __builtin_amdgcn_sched_barrier(0);   // the wait below must not rise above the MFMAs
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of step ks + 1 have landed
-        __syncthreads();                 // ... everyone's, and step ks's buffers are free
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(fa[1], fw[1]);
     }
 
     // ---- epilogue: accumulator (lane, r) -> row 8(r/4) + 4(lane/32) + r%4, col lane%32
