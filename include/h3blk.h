@@ -105,7 +105,7 @@ h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim,
  *   A : [M][K] with row stride lda (elements)
  *   W : [N][K] with row stride ldw (weights stored out-features major)
  *   C : [M][N] with row stride ldc; must not overlap A or W
- * bf16: K a multiple of 32; fp32: K a multiple of 16; N a multiple of 8.
+ * bf16: K a multiple of 64; fp32: K a multiple of 32; N a multiple of 8.
  * Accumulation is fp32 in MFMA; C is rounded once. */
 h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw,
                        void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,

@@ -99,7 +99,7 @@ h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, v
     if (!A || !W || !C || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
     const int es = esize(dt);
     if (lda < K || ldw < K || ldc < N) return H3_ERR_ARG;
-    if (M >= kMaxTok || N % 8 || K % (dt == H3_BF16 ? 32 : 16)) return H3_ERR_SHAPE;
+    if (M >= kMaxTok || N % 8 || K % (dt == H3_BF16 ? 64 : 32)) return H3_ERR_SHAPE;
     // a 256-row operand tile is addressed with 32-bit byte offsets
     if (lda * es * 256 >= ((int64_t)1 << 31) || ldw * es * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
     if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (lda * es) % 16 || (ldw * es) % 16 ||
