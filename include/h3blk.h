@@ -137,7 +137,7 @@ h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok,
  *   o       : [n_tok][heads*head_dim] with row stride ld_o (must not alias q/k/v)
  *   lse     : optional fp32 [heads][n_tok], receives
  *             log(sum_j exp(scale * q[i,h] . k[j,h])) (natural log); NULL to skip
- * head_dim in {64, 128}; n_tok < 2^31. */
+ * head_dim in {64, 128}; n_tok < 2^31; scale finite and > 0. */
 h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv,
                            void* o, int64_t ld_o, int64_t n_tok, int32_t heads,
                            int32_t head_dim, float scale, float* lse,

@@ -162,6 +162,8 @@ def test_attention_validation(lib):
     assert a(o=q) == blk.H3_ERR_ARG
     assert a(ldo=100) == blk.H3_ERR_ARG
     assert a(scale=float("inf")) == blk.H3_ERR_ARG
+    assert a(scale=0.0) == blk.H3_ERR_ARG       # masked keys are -inf logits: the scale must be > 0
+    assert a(scale=-0.088) == blk.H3_ERR_ARG
     assert a(lse=P + 2) == blk.H3_ERR_ALIGN
     assert a(ld=1 << 24) == blk.H3_ERR_SHAPE
     assert a(q=q + 8) == blk.H3_ERR_ALIGN

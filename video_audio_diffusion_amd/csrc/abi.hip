@@ -158,7 +158,7 @@ h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t 
                            int64_t n_tok, int32_t heads, int32_t head_dim, float scale, float* lse,
                            h3_dtype dt, void* stream) {
     if (!valid_dt(dt)) return H3_ERR_DTYPE;
-    if (!q || !k || !v || !o || n_tok < 0 || heads < 1 || !isfinite(scale)) return H3_ERR_ARG;
+    if (!q || !k || !v || !o || n_tok < 0 || heads < 1 || !isfinite(scale) || !(scale > 0.f)) return H3_ERR_ARG;
     if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
     const int es = esize(dt);
     const int64_t width = (int64_t)heads * head_dim;

@@ -36,6 +36,8 @@
 // work while the exponentials run.
 #include "launch.h"
 
+#include <type_traits>
+
 namespace h3 {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -63,6 +65,9 @@ template <> struct AttnMfma<float> {
 };
 
 constexpr int kAttnWaves = 8;
+#ifndef H3_ATTN_TB
+#define H3_ATTN_TB 2    // 32-key blocks per LDS tile of the pipelined bf16 kernel
+#endif
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kBQ = kAttnWaves * 32;         // 256 queries per workgroup
 // The reference max of a query only moves when a block's max exceeds it by
@@ -70,6 +75,10 @@ constexpr int kBQ = kAttnWaves * 32;         // 256 queries per workgroup
 // rescale is skipped for most blocks; the result is unchanged because the
 // final division uses the same reference.
 constexpr float kLazyMax = 8.0f;
+// Pipelined kernel: largest row sum of one block's exponentials (per lane, 16
+// keys) accepted against the current reference before it is raised.  Bounds
+// every exponential by 2^20, far inside fp32 range for the sums and outputs.
+constexpr float kRedoSum = 1048576.0f;
 
 // 16-byte chunk c of the row of key `key` sits at chunk c ^ swz(key).
 template <int CH> __device__ __forceinline__ int kswz(int key) { return key & (CH >= 16 ? 15 : CH - 1); }
@@ -83,7 +92,10 @@ template <int IPW, int TILE, typename T>
 __device__ __forceinline__ void copy_kv_tile(char* buf, int wave, const T* Kp, const T* Vp, int64_t hoff, int kv0,
                                              int n, int bkv, int64_t ld, uint32_t ldb, const uint32_t* dk,
                                              const uint32_t* dv) {
-    const int nvalid = n - kv0 < bkv ? n - kv0 : bkv;
+    const int rem = n - kv0;
+    // tiles past the end read as zeros; readfirstlane keeps the descriptor in
+    // scalar registers (a clamp evaluated on the VALU would make it look divergent)
+    const int nvalid = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem < bkv ? rem : bkv));
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
 #pragma unroll
@@ -93,6 +105,25 @@ __device__ __forceinline__ void copy_kv_tile(char* buf, int wave, const T* Kp, c
     for (int i = 0; i < IPW; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(buf + TILE + (wave * IPW + i) * 1024), 16, dv[i], 0, 0,
                                                  0);
+}
+
+// The same copy with the K and V tiles in separate LDS buffers.
+template <int IPW>
+__device__ __forceinline__ void copy_kv_tile2(char* kbuf, char* vbuf, int wave, const bf16* Kp, const bf16* Vp,
+                                              int64_t hoff, int kv0, int n, int bkv, int64_t ld, uint32_t ldb,
+                                              const uint32_t* dk, const uint32_t* dv) {
+    const int rem = n - kv0;
+    // tiles past the end read as zeros; readfirstlane keeps the descriptor in
+    // scalar registers (a clamp evaluated on the VALU would make it look divergent)
+    const int nvalid = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem < bkv ? rem : bkv));
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vp + (int64_t)kv0 * ld + hoff, (uint32_t)nvalid * ldb);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, H3_LDS(kbuf + (wave * IPW + i) * 1024), 16, dk[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(vbuf + (wave * IPW + i) * 1024), 16, dv[i], 0, 0, 0);
 }
 
 template <typename T, int HD>
@@ -322,6 +353,301 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
     }
 }
 
+// ---------------------------------------------------------------- bf16: pipelined key sweep
+// Same work split (8 wavefronts x 32 queries) and fragment layouts as above;
+// the key sweep of each wavefront is software-pipelined over 32-key blocks.
+// Iteration j runs sixteen MFMA slots -- QK of block j+1 (one per 32-byte
+// chunk of head_dim), then PV of block j (one per d block and key half) --
+// and every slot carries its share of the VALU work of the softmax
+// (exponentials of block j in the QK slots, the row sum and the max of block
+// j+1 in the PV slots) and of the LDS reads for the next iteration.  The
+// slots are fenced from one another (sched_barrier), which fixes the
+// interleave -- a wavefront's own independent VALU instructions are what
+// issue while its MFMAs execute -- and keeps every fragment register reused
+// chunk by chunk.
+//
+// LDS: [K | V] tiles of 64 keys (2 blocks) in two buffers, so that every
+// fragment address is a per-lane base plus an immediate offset.  K
+// fragments of block b are read in iteration b-1 when b starts a tile and
+// in iteration b-2 otherwise; V^T fragments in iteration b-1.  Tile u is
+// therefore read in iterations 2u-1 and 2u, and one barrier per tile, before
+// iteration 2u+1, makes tile u+1 visible (its copies went out one barrier
+// earlier) and frees tile u's buffer for the copy of tile u+2.
+template <int HD, int TB>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int64_t ld,
+    bf16* __restrict__ O, int64_t ldo, int32_t n, int32_t heads, float sl2, float* __restrict__ lse,
+    int32_t nqt) {
+    constexpr int RB = HD * 2;                   // bytes of one K or V row
+    constexpr int CH = RB / 16;                  // 16-byte chunks per row
+    constexpr int BKV = 32 * TB;                 // keys per tile (TB blocks)
+    constexpr int TILE = BKV * RB;               // bytes of one operand tile
+    constexpr int IPW = TILE / (1024 * kAttnWaves);
+    constexpr int NCH = RB / 32;                 // QK MFMAs per block
+    constexpr int DB = HD / 32;                  // 32-wide d blocks of the output
+    constexpr int NPV = 2 * DB;                  // PV MFMAs per block
+    static_assert(IPW >= 1 && TILE % (1024 * kAttnWaves) == 0, "tile split");
+    static_assert(16 % NCH == 0, "exponentials spread evenly over the QK slots");
+
+    // Two K and two V tile buffers, declared in this order so that each
+    // operand's pair lies in one 64 KB window: a fragment address is then a
+    // per-lane base plus an immediate offset for either buffer.
+    __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+
+    const int G = heads * nqt;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, local = b >> 3;
+    const int base = G >> 3, extra = G & 7;
+    const int L = xcd * base + (xcd < extra ? xcd : extra) + local;
+    const int head = L / nqt;
+    const int qt = L - head * nqt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int q0 = qt * kBQ + wave * 32;
+    const int64_t hoff = (int64_t)head * HD;
+    const uint32_t ldb = (uint32_t)(ld * 2);
+
+    u32x4 qf[NCH];
+    {
+        const int qi = q0 + col;
+        const char* src = reinterpret_cast<const char*>(Q + (int64_t)(qi < n ? qi : n - 1) * ld + hoff);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(src + c * 32 + g * 16);
+    }
+    uint32_t ko[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) ko[c] = (uint32_t)(col * RB + (((2 * c + g) ^ kswz<CH>(col)) << 4));
+    uint32_t vo[DB];
+    {
+        const int q = lane >> 4, r = (lane >> 2) & 3, a = lane & 3;
+        const int kr = 4 * (q >> 1) + r;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int c = 4 * db + 2 * (q & 1) + (a >> 1);
+            vo[db] = (uint32_t)(kr * RB + ((c ^ vswz<CH>(kr)) << 4) + (a & 1) * 8);
+        }
+    }
+
+    // Hide the offsets' value range from the compiler: otherwise it proves
+    // offset and block displacement bit-disjoint and builds each address with
+    // a v_or instead of the instruction's immediate offset.
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(ko[c]));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(vo[db]));
+
+    const int NB = (n + 31) >> 5;    // 32-key blocks
+    const int NBF = n >> 5;          // blocks with 32 valid keys
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+    float m_ref, l_run = 0.f;
+    f32x16 s;              // logits of the block whose softmax is next
+    u32x4 kf[NCH];         // K fragments of the next QK
+    u32x4 vf[DB][2];       // V^T fragments of the next PV
+
+    // LDS copy of tile t into kb / vb (lane offsets recomputed: they serve once per tile)
+    auto copy_tile = [&](char* kb, char* vb, int t) __attribute__((always_inline)) {
+        uint32_t dk[IPW], dv[IPW];
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int p = 64 * (wave * IPW + i) + lane;
+            const int key = p / CH, ph = p % CH;
+            dk[i] = (uint32_t)key * ldb + (uint32_t)((ph ^ kswz<CH>(key)) << 4);
+            dv[i] = (uint32_t)key * ldb + (uint32_t)((ph ^ vswz<CH>(key)) << 4);
+        }
+        copy_kv_tile2<IPW>(kb, vb, wave, Kp, Vp, hoff, t * BKV, n, BKV, ld, ldb, dk, dv);
+    };
+    auto read_k1 = [&](const char* buf, int blk, int c) __attribute__((always_inline)) {
+        kf[c] = *reinterpret_cast<const u32x4*>(buf + blk * 32 * RB + ko[c]);
+    };
+    auto read_v1 = [&](const char* buf, int blk, int db, int h) __attribute__((always_inline)) {
+        const char* vp = buf + blk * 32 * RB + 16 * h * RB + vo[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp + 8 * RB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        vf[db][h] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
+    };
+    auto mask = [&](f32x16& acc, int kbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (kbase + 8 * (r >> 2) + 4 * g + (r & 3) >= n) acc[r] = -__builtin_inff();
+    };
+    // scaled max of a block for this lane's query (both lane halves)
+    auto block_max = [&](const f32x16& a) __attribute__((always_inline)) -> float {
+        float mx = __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, a[r]), a[r + 1]);
+        mx = __builtin_fmaxf(mx, a[15]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+    };
+    // Exponentials of block j under the current reference, packed as bf16
+    // pairs (the B operand of PV); rs = their row sum over this lane's 16 keys,
+    // taken from the packed values with v_dot2 (the weights PV sees).
+    auto softmax_exp = [&](u32x4 (&pfr)[2], float& rs) __attribute__((always_inline)) {
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+        rs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[r], sl2, -m_ref));
+            const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], sl2, -m_ref));
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pfr[r >> 3][(r >> 1) & 3] = w;
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, rs, false);
+        }
+    };
+
+    // One iteration.  Blocks past the last key are zero-filled by the tile
+    // copies and masked to -inf here, so the sweep may run a few blocks past
+    // the end at no cost to the result: every block it touches exists.
+    // Only the last trips test for that (CHECK).
+    //
+    // Reference: the exponentials of block j are taken against the current
+    // reference without first computing the block max; only if some query's
+    // row sum over the block comes out above kRedoSum (or not finite) is the
+    // block max taken, the reference raised, the output and sum rescaled and
+    // the exponentials redone.  Every exponential the sums and PV see is
+    // therefore at most kRedoSum, and the result is the same softmax: the
+    // final division uses the same reference.
+    //
+    // JIT: read block j+1's K fragments first; PF: prefetch block j+2's K
+    // fragments behind the QK slots.  b1/b2: LDS block of j+1 / j+2 in its tile.
+    auto step = [&](int j, auto jit, auto pf, auto chk, int b1, int b2, const char* kbj, const char* vb,
+                    const char* kbp) __attribute__((always_inline)) {
+        constexpr bool JIT = decltype(jit)::value;
+        constexpr bool PF = decltype(pf)::value;
+        constexpr bool CHECK = decltype(chk)::value;   // block j+1 may hold keys past the end
+        if (JIT) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) read_k1(kbj, b1, c);
+        }
+        f32x16 sn = (f32x16){};
+        u32x4 pfr[2];
+        float rs;
+        // ---- QK of block j+1 and its K prefetch, exponentials of block j
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                         __builtin_bit_cast(bf16x8, qf[c]), sn, 0, 0, 0);
+            if (PF) read_k1(kbp, b2, c);
+        }
+        softmax_exp(pfr, rs);
+        // Issue order: each QK MFMA with one K read and its share of the
+        // exponentials (fma, exp, fma, exp, pack, dot2).
+        if (JIT) __builtin_amdgcn_sched_group_barrier(0x100, NCH, 0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 48 / NCH, 0);
+        }
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kRedoSum)) != 0, 0)) {   // rare: raise the reference
+            const float mx = block_max(s);
+            const float m_new = __builtin_fmaxf(m_ref, mx);
+            const float alpha = fast_exp2(m_ref - m_new);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            l_run *= alpha;
+            m_ref = m_new;
+            softmax_exp(pfr, rs);
+        }
+        // ---- PV of block j, V^T fragments of block j+1
+#pragma unroll
+        for (int k = 0; k < NPV; ++k) {
+            const int db = k >> 1, h = k & 1;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[db][h]),
+                                                               __builtin_bit_cast(bf16x8, pfr[h]), oacc[db], 0, 0, 0);
+            read_v1(vb, b1, db, h);
+        }
+        l_run += rs;
+        if (CHECK && __builtin_expect(j + 1 >= NBF, 0)) mask(sn, (j + 1) * 32);
+        s = sn;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // Barrier before iteration TB*u + TB-1: tile u+1 visible, then the copy
+    // of tile u+2 into tile u's buffer.
+    auto tile_barrier = [&](int u, char* free_k, char* free_v) __attribute__((always_inline)) {
+        wait_vm<0, true>();
+        __builtin_amdgcn_s_barrier();
+        if (TB * (u + 2) < NB) copy_tile(free_k, free_v, u + 2);
+    };
+    // Iterations j .. j + 2TB-1 for j = 2TB*w + TB-1: tiles u+1 (buffer 1)
+    // and u+2 (buffer 0), u = 2w.
+    auto trip = [&](int j, auto chk) __attribute__((always_inline)) {
+        const int u = (j - (TB - 1)) / TB;
+#pragma unroll
+        for (int i = 0; i < 2 * TB; ++i) {
+            char* rk = i < TB ? k_lds1 : k_lds0;
+            char* rv = i < TB ? v_lds1 : v_lds0;
+            if (i == 0) tile_barrier(u, k_lds0, v_lds0);
+            if (i == TB) tile_barrier(u + 1, k_lds1, v_lds1);
+            const int b1 = i % TB, b2 = (i + 1) % TB;
+            if (b1 == 0) step(j + i, T_{}, T_{}, chk, b1, b2, rk, rv, rk);
+            else if (b2 != 0) step(j + i, F_{}, T_{}, chk, b1, b2, rk, rv, rk);
+            else step(j + i, F_{}, F_{}, chk, b1, b2, rk, rv, rk);
+        }
+    };
+
+    // ---- prologue: tiles 0 and 1 in flight, block 0's logits and V^T, block 1's K
+    __builtin_amdgcn_s_waitcnt(0);
+    copy_tile(k_lds0, v_lds0, 0);
+    copy_tile(k_lds1, v_lds1, 1);
+    wait_vm<2 * IPW, true>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 0, c);
+    s = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]), __builtin_bit_cast(bf16x8, qf[c]),
+                                                   s, 0, 0, 0);
+    if (NBF == 0) mask(s, 0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) read_v1(v_lds0, 0, db, h);
+    m_ref = block_max(s);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 1, c);
+    // iterations 0 .. TB-2 read tile 0 only (the K of block TB is read just in time)
+#pragma unroll
+    for (int i = 0; i + 1 < TB; ++i) {
+        if (i + 2 < TB) step(i, F_{}, T_{}, T_{}, i + 1, i + 2, k_lds0, v_lds0, k_lds0);
+        else step(i, F_{}, F_{}, T_{}, i + 1, 0, k_lds0, v_lds0, k_lds0);
+    }
+    int j = TB - 1;
+    for (; j + 2 * TB < NBF; j += 2 * TB) trip(j, F_{});   // blocks up to j + 2TB complete
+    for (; j < NB; j += 2 * TB) trip(j, T_{});
+    wait_vm<0, true>();    // no tile copy may land after the workgroup's LDS is released
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    const float inv = 1.0f / l_tot;
+    const int qi = q0 + col;
+    if (qi < n) {
+        bf16* orow = O + (int64_t)qi * ldo + hoff;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                const f32x16& a = oacc[db];
+                *reinterpret_cast<u32x2*>(orow + d) =
+                    (u32x2){pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
+                            pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
+            }
+        if (lse && g == 0) lse[(int64_t)head * n + qi] = m_ref * 0.69314718055994531f + __logf(l_tot);
+    }
+}
+
 hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v, int64_t ld, void* o,
                             int64_t ldo, int32_t n, int32_t heads, int32_t hd, float scale, float* lse,
                             hipStream_t st) {
@@ -332,8 +658,12 @@ hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v
     attn_fwd_kernel<TY, D><<<grid, kAttnThreads, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld,  \
                                                           (TY*)o, ldo, n, heads, sl2, lse, nqt)
     if (bf) {
-        if (hd == 128) H3_ATTN(bf16, 128);
-        else H3_ATTN(bf16, 64);
+        if (hd == 128)
+            attn_bf16_kernel<128, H3_ATTN_TB><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+                                                                  (bf16*)o, ldo, n, heads, sl2, lse, nqt);
+        else
+            attn_bf16_kernel<64, H3_ATTN_TB><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+                                                                 (bf16*)o, ldo, n, heads, sl2, lse, nqt);
     } else {
         if (hd == 128) H3_ATTN(float, 128);
         else H3_ATTN(float, 64);

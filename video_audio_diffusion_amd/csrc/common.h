@@ -99,6 +99,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// s_waitcnt immediate: at most n vector-memory operations of this wavefront
+// outstanding and, with lgkm0, no LDS operation outstanding (the expcnt
+// field is left unconstrained).
+template <int n, bool lgkm0>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((((n >> 4) & 3) << 14) | ((lgkm0 ? 0 : 0xF) << 8) | (0x7 << 4) | (n & 15));
+}
+
 #define H3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 }  // namespace h3

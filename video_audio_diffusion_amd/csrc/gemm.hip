@@ -52,15 +52,6 @@ template <> struct GemmMfma<float> {
 
 constexpr int kBM = 256, kBN = 256;
 
-// s_waitcnt immediate: at most n vector-memory operations of this wavefront
-// outstanding and, with lgkm0, no LDS operation outstanding (the expcnt
-// field is left unconstrained).
-template <int n, bool lgkm0>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((((n >> 4) & 3) << 14) | ((lgkm0 ? 0 : 0xF) << 8) | (0x7 << 4) | (n & 15));
-}
-
 // Tile geometry for ROWB bytes of K per step (64 or 128) and a STAGES-deep
 // LDS ring.  Rows of ROWB bytes hold CPR 16-byte chunks; 256 / ROWB rows
 // share one 256-byte bank window, so chunk c of row r is stored at
