@@ -65,9 +65,6 @@ template <> struct AttnMfma<float> {
 };
 
 constexpr int kAttnWaves = 8;
-#ifndef H3_ATTN_TB
-#define H3_ATTN_TB 2    // 32-key blocks per LDS tile of the pipelined bf16 kernel
-#endif
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kBQ = kAttnWaves * 32;         // 256 queries per workgroup
 // The reference max of a query only moves when a block's max exceeds it by
@@ -356,31 +353,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
 // ---------------------------------------------------------------- bf16: pipelined key sweep
 // Same work split (8 wavefronts x 32 queries) and fragment layouts as above;
 // the key sweep of each wavefront is software-pipelined over 32-key blocks.
-// Iteration j runs sixteen MFMA slots -- QK of block j+1 (one per 32-byte
-// chunk of head_dim), then PV of block j (one per d block and key half) --
-// and every slot carries its share of the VALU work of the softmax
-// (exponentials of block j in the QK slots, the row sum and the max of block
-// j+1 in the PV slots) and of the LDS reads for the next iteration.  The
-// slots are fenced from one another (sched_barrier), which fixes the
-// interleave -- a wavefront's own independent VALU instructions are what
-// issue while its MFMAs execute -- and keeps every fragment register reused
-// chunk by chunk.
+// Iteration j issues QK of block j+1 (one MFMA per 32-byte chunk of
+// head_dim) interleaved with the exponentials of block j, then PV of block
+// j (one MFMA per d block and key half) with the V^T reads of block j+1, all
+// in one basic block: a wavefront's own independent VALU instructions are
+// what issue while its MFMAs execute.
 //
-// LDS: [K | V] tiles of 64 keys (2 blocks) in two buffers, so that every
+// LDS: K and V tiles of 64 keys (2 blocks) in a ring of three buffers per
+// operand, each operand's three buffers declared together so that every
 // fragment address is a per-lane base plus an immediate offset.  K
-// fragments of block b are read in iteration b-1 when b starts a tile and
-// in iteration b-2 otherwise; V^T fragments in iteration b-1.  Tile u is
-// therefore read in iterations 2u-1 and 2u, and one barrier per tile, before
-// iteration 2u+1, makes tile u+1 visible (its copies went out one barrier
-// earlier) and frees tile u's buffer for the copy of tile u+2.
-template <int HD, int TB>
+// fragments of block b are read in iteration b-2, V^T fragments in iteration
+// b-1, so tile u is read in iterations 2u-2 .. 2u.  One barrier per tile,
+// before iteration 2u, makes tile u+1 visible (its copies went out one
+// barrier earlier) and frees the buffer of tile u-1, whose reads ended in
+// iteration 2u-2, for the copy of tile u+2.
+template <int HD>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int64_t ld,
     bf16* __restrict__ O, int64_t ldo, int32_t n, int32_t heads, float sl2, float* __restrict__ lse,
     int32_t nqt) {
     constexpr int RB = HD * 2;                   // bytes of one K or V row
     constexpr int CH = RB / 16;                  // 16-byte chunks per row
-    constexpr int BKV = 32 * TB;                 // keys per tile (TB blocks)
+    constexpr int BKV = 64;                      // keys per tile (2 blocks)
     constexpr int TILE = BKV * RB;               // bytes of one operand tile
     constexpr int IPW = TILE / (1024 * kAttnWaves);
     constexpr int NCH = RB / 32;                 // QK MFMAs per block
@@ -389,13 +383,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     static_assert(IPW >= 1 && TILE % (1024 * kAttnWaves) == 0, "tile split");
     static_assert(16 % NCH == 0, "exponentials spread evenly over the QK slots");
 
-    // Two K and two V tile buffers, declared in this order so that each
-    // operand's pair lies in one 64 KB window: a fragment address is then a
-    // per-lane base plus an immediate offset for either buffer.
+    // Three K then three V tile buffers: each operand's ring lies in one
+    // window of less than 64 KB.  Separate objects let the compiler see that
+    // a copy into one buffer leaves reads of the others free to proceed.
     __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds2[TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds2[TILE];
+    auto kbuf = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? k_lds0 : i == 1 ? k_lds1 : k_lds2; };
+    auto vbuf = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? v_lds0 : i == 1 ? v_lds1 : v_lds2; };
 
     const int G = heads * nqt;
     const int b = blockIdx.x;
@@ -506,9 +504,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     };
 
     // One iteration.  Blocks past the last key are zero-filled by the tile
-    // copies and masked to -inf here, so the sweep may run a few blocks past
-    // the end at no cost to the result: every block it touches exists.
-    // Only the last trips test for that (CHECK).
+    // copies (or stale) and masked to -inf here, so the sweep may run a few
+    // blocks past the end at no cost to the result.  Only the last trips test
+    // for that (CHECK).
     //
     // Reference: the exponentials of block j are taken against the current
     // reference without first computing the block max; only if some query's
@@ -518,35 +516,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     // therefore at most kRedoSum, and the result is the same softmax: the
     // final division uses the same reference.
     //
-    // JIT: read block j+1's K fragments first; PF: prefetch block j+2's K
-    // fragments behind the QK slots.  b1/b2: LDS block of j+1 / j+2 in its tile.
-    auto step = [&](int j, auto jit, auto pf, auto chk, int b1, int b2, const char* kbj, const char* vb,
-                    const char* kbp) __attribute__((always_inline)) {
-        constexpr bool JIT = decltype(jit)::value;
-        constexpr bool PF = decltype(pf)::value;
+    // kp/b2: buffer and block of block j+2's K (prefetched); vb/b1: those of
+    // block j+1's V^T.
+    auto step = [&](int j, auto chk, const char* kp, int b2, const char* vb, int b1) __attribute__((always_inline)) {
         constexpr bool CHECK = decltype(chk)::value;   // block j+1 may hold keys past the end
-        if (JIT) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) read_k1(kbj, b1, c);
-        }
         f32x16 sn = (f32x16){};
         u32x4 pfr[2];
         float rs;
-        // ---- QK of block j+1 and its K prefetch, exponentials of block j
+        // ---- QK of block j+1 and block j+2's K reads, exponentials of block j
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
                                                          __builtin_bit_cast(bf16x8, qf[c]), sn, 0, 0, 0);
-            if (PF) read_k1(kbp, b2, c);
+            read_k1(kp, b2, c);
         }
         softmax_exp(pfr, rs);
         // Issue order: each QK MFMA with one K read and its share of the
         // exponentials (fma, exp, fma, exp, pack, dot2).
-        if (JIT) __builtin_amdgcn_sched_group_barrier(0x100, NCH, 0);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 48 / NCH, 0);
         }
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kRedoSum)) != 0, 0)) {   // rare: raise the reference
@@ -573,36 +563,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // Barrier before iteration TB*u + TB-1: tile u+1 visible, then the copy
-    // of tile u+2 into tile u's buffer.
+    // Barrier before iteration 2u: this wavefront's copies of tile u+1 have
+    // landed, then everyone's have; tile u-1's buffer takes tile u+2.  No LDS
+    // read needs draining: the last reads of tile u-1 were in iteration 2u-2.
     auto tile_barrier = [&](int u, char* free_k, char* free_v) __attribute__((always_inline)) {
-        wait_vm<0, true>();
+        wait_vm<0, false>();
         __builtin_amdgcn_s_barrier();
-        if (TB * (u + 2) < NB) copy_tile(free_k, free_v, u + 2);
+        if (2 * (u + 2) < NB) copy_tile(free_k, free_v, u + 2);
     };
-    // Iterations j .. j + 2TB-1 for j = 2TB*w + TB-1: tiles u+1 (buffer 1)
-    // and u+2 (buffer 0), u = 2w.
+    // Iterations j .. j+5 for j = 6w + 2 (tiles 3w+1 .. 3w+4): ring
+    // positions are compile-time constants.
     auto trip = [&](int j, auto chk) __attribute__((always_inline)) {
-        const int u = (j - (TB - 1)) / TB;
+        const int u = j >> 1;
 #pragma unroll
-        for (int i = 0; i < 2 * TB; ++i) {
-            char* rk = i < TB ? k_lds1 : k_lds0;
-            char* rv = i < TB ? v_lds1 : v_lds0;
-            if (i == 0) tile_barrier(u, k_lds0, v_lds0);
-            if (i == TB) tile_barrier(u + 1, k_lds1, v_lds1);
-            const int b1 = i % TB, b2 = (i + 1) % TB;
-            if (b1 == 0) step(j + i, T_{}, T_{}, chk, b1, b2, rk, rv, rk);
-            else if (b2 != 0) step(j + i, F_{}, T_{}, chk, b1, b2, rk, rv, rk);
-            else step(j + i, F_{}, F_{}, chk, b1, b2, rk, rv, rk);
+        for (int i = 0; i < 6; ++i) {
+            if ((i & 1) == 0) tile_barrier(u + i / 2, kbuf((i / 2) % 3), vbuf((i / 2) % 3));
+            step(j + i, chk, kbuf(((4 + i) / 2) % 3), i & 1, vbuf(((3 + i) / 2) % 3), (i + 1) & 1);
         }
     };
 
-    // ---- prologue: tiles 0 and 1 in flight, block 0's logits and V^T, block 1's K
+    // ---- prologue: tiles 0 and 1 visible, tile 2 in flight; block 0's
+    //      logits and V^T, block 1's K
     __builtin_amdgcn_s_waitcnt(0);
     copy_tile(k_lds0, v_lds0, 0);
     copy_tile(k_lds1, v_lds1, 1);
-    wait_vm<2 * IPW, true>();
+    wait_vm<0, false>();
     __builtin_amdgcn_s_barrier();
+    if (4 < NB) copy_tile(k_lds2, v_lds2, 2);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 0, c);
     s = (f32x16){};
@@ -618,15 +605,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     m_ref = block_max(s);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 1, c);
-    // iterations 0 .. TB-2 read tile 0 only (the K of block TB is read just in time)
-#pragma unroll
-    for (int i = 0; i + 1 < TB; ++i) {
-        if (i + 2 < TB) step(i, F_{}, T_{}, T_{}, i + 1, i + 2, k_lds0, v_lds0, k_lds0);
-        else step(i, F_{}, F_{}, T_{}, i + 1, 0, k_lds0, v_lds0, k_lds0);
-    }
-    int j = TB - 1;
-    for (; j + 2 * TB < NBF; j += 2 * TB) trip(j, F_{});   // blocks up to j + 2TB complete
-    for (; j < NB; j += 2 * TB) trip(j, T_{});
+    step(0, T_{}, k_lds1, 0, v_lds0, 1);
+    step(1, T_{}, k_lds1, 1, v_lds1, 0);
+    int j = 2;
+    for (; j + 6 < NBF; j += 6) trip(j, F_{});   // blocks up to j + 6 complete
+    for (; j < NB; j += 6) trip(j, T_{});
     wait_vm<0, true>();    // no tile copy may land after the workgroup's LDS is released
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -659,10 +642,10 @@ hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v
                                                           (TY*)o, ldo, n, heads, sl2, lse, nqt)
     if (bf) {
         if (hd == 128)
-            attn_bf16_kernel<128, H3_ATTN_TB><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+            attn_bf16_kernel<128><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                                                   (bf16*)o, ldo, n, heads, sl2, lse, nqt);
         else
-            attn_bf16_kernel<64, H3_ATTN_TB><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+            attn_bf16_kernel<64><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                                                  (bf16*)o, ldo, n, heads, sl2, lse, nqt);
     } else {
         if (hd == 128) H3_ATTN(float, 128);

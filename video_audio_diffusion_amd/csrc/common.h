@@ -108,6 +108,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((((n >> 4) & 3) << 14) | ((lgkm0 ? 0 : 0xF) << 8) | (0x7 << 4) | (n & 15));
 }
 
+// s_waitcnt immediate: at most vm vector-memory and lgkm LDS operations of
+// this wavefront outstanding.
+template <int vm, int lgkm>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(vm >= 0 && vm < 64 && lgkm >= 0 && lgkm < 16, "count range");
+    __builtin_amdgcn_s_waitcnt((((vm >> 4) & 3) << 14) | (lgkm << 8) | (0x7 << 4) | (vm & 15));
+}
+
 #define H3_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 }  // namespace h3
