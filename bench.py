@@ -128,12 +128,36 @@ def cpu_baseline(cfg, host, target_s):
                       f"(their own q/k/v included) against a full {N}-key K/V; {el:.1f} s wall"}
 
 
+def device_block_weights(cfg, b):
+    """Random-init weights of block b of a stack, drawn on the device (torch's
+    generator seeded per block and tensor; 770 MB per full-width block, so
+    the host draws of the single-block workloads would take minutes)."""
+    import torch
+
+    from video_audio_diffusion_amd import inputs
+    from video_audio_diffusion_amd.block import BlockWeights
+
+    D, I, F = cfg.dim, cfg.inner, cfg.ffn
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def rnd(name, shape, std, dtype):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(inputs.stack_seed(cfg.index, b, name))
+        return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std).to(dtype)
+
+    gain = torch.full((cfg.head_dim,), cfg.gamma, device="cuda", dtype=torch.float32)
+    return BlockWeights(rnd("w_qkv", (3 * I, D), cfg.w_std, wdt), rnd("w_o", (D, I), cfg.w_std, wdt),
+                        rnd("w_gu", (2 * F, D), cfg.w_std, wdt), rnd("w_d", (D, F), cfg.w_std, wdt),
+                        rnd("mod", (inputs.N_MOD_SETS, inputs.N_MOD_CHUNKS, D), 1.0, torch.float32), gain, gain)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload index (1-4)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index: 1-4 one block; 5 the 50-block stack and one Euler step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget; 0 skips it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -145,40 +169,66 @@ def main():
     import torch
 
     from video_audio_diffusion_amd import blk, inputs
-    from video_audio_diffusion_amd.block import BlockWeights, H3Block, device_inputs
+    from video_audio_diffusion_amd.block import BlockWeights, H3Block, H3Stack, device_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     blk.load()
-    cfg = inputs.CONFIGS[args.config]
-    log(f"workload {cfg.name}: {cfg.n_tok} tokens; drawing inputs")
-    host = inputs.make_inputs(cfg)
-    dev = device_inputs(cfg, host)
-    log("inputs resident on device")
-    block = H3Block(cfg, BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
-                                      dev["gamma_q"], dev["gamma_k"]))
+    stack = None
+    if args.config in inputs.STACKS:
+        scfg = inputs.STACKS[args.config]
+        cfg = scfg.block
+        log(f"workload {scfg.name}: {scfg.n_blocks} blocks, {cfg.n_tok} tokens; drawing weights on device")
+        host = inputs.make_inputs(cfg, ("x",))
+        dev = device_inputs(cfg, host)
+        stack = H3Stack(scfg, [device_block_weights(cfg, b) for b in range(scfg.n_blocks)])
+        log("weights resident on device")
+        n_blk = scfg.n_blocks
+    else:
+        cfg = inputs.CONFIGS[args.config]
+        log(f"workload {cfg.name}: {cfg.n_tok} tokens; drawing inputs")
+        host = inputs.make_inputs(cfg)
+        dev = device_inputs(cfg, host)
+        log("inputs resident on device")
+        block = H3Block(cfg, BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
+                                          dev["gamma_q"], dev["gamma_k"]))
+        n_blk = 1
     x = dev["x"]
+
+    def one_step(events):
+        """One timed pass: `events` holds 12 events per block and one more
+        recorded after the pass."""
+        if stack is None:
+            block.forward(x, events=events[0])
+        else:
+            stack.forward(x, block_events=events)
+        events[-1][0].record()
+
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(n_blk)] + \
+        [[torch.cuda.Event(enable_timing=True)]]
     for i in range(args.warmup):
-        block.forward(x)
+        one_step(new_events())
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup} done")
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(K)]
+    ev = [new_events() for _ in range(K)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(K):
-        block.forward(x, events=ev[i])
+        one_step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    total_ms = ev[0][0].elapsed_time(ev[K - 1][11])
+    total_ms = ev[0][0][0].elapsed_time(ev[K - 1][-1][0])
     ms_step = total_ms / K
     log(f"timed {K} steps: {ms_step:.2f} ms/step (host wall {wall * 1e3 / K:.2f} ms/step)")
 
-    per = {name: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+    # per-kernel time of one pass (summed over the blocks of a stack)
+    per = {name: sum(ev[i][b][j].elapsed_time(ev[i][b][j + 1]) for i in range(K) for b in range(n_blk)) / K
            for j, name in enumerate(H3Block.STEPS)}
-    flops, byts = step_flops(cfg), step_bytes(cfg)
+    flops = {k: v * n_blk for k, v in step_flops(cfg).items()}
+    byts = {k: v * n_blk for k, v in step_bytes(cfg).items()}
     peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {}
     for name, ms in per.items():
@@ -197,7 +247,9 @@ def main():
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": f"{cfg.name} block forward", "tokens": cfg.n_tok,
+        "config": {"workload": (f"{cfg.name} block forward" if stack is None else
+                                f"{inputs.STACKS[args.config].name}: {n_blk} blocks and one Euler step"),
+                   "blocks": n_blk, "tokens": cfg.n_tok,
                    "segments": [f"{s.kind} {s.T}x{s.H}x{s.W}" for s in cfg.segments],
                    "hidden": cfg.dim, "heads": cfg.heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
                    "rope_split": list(cfg.rope_split), "global_batch": 1, "seq_len": cfg.n_tok,
@@ -207,10 +259,10 @@ def main():
         "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(attn_tf, 1), "peak": peak_mm,
                      "unit": "TFLOP/s", "frac": round(attn_tf / peak_mm, 4),
                      "traffic": measured_traffic("attention"),
-                     "algorithmic_per_launch": f"{flops['attention']:.4e} flop (4*N^2*heads*head_dim)"},
+                     "algorithmic_per_launch": f"{flops['attention'] / n_blk:.4e} flop (4*N^2*heads*head_dim)"},
         "cpu_baseline": None,
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and stack is None:
         log("timing the fp64 oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(cfg, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)

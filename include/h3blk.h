@@ -160,6 +160,19 @@ h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_to
                            const h3_segment* segs, int32_t n_segs,
                            h3_dtype dt, void* stream);
 
+/* Euler step of the flow sampler, in place ([notes] section 6: video and
+ * audio follow separately configured shifted schedules and each receives an
+ * Euler update from its velocity prediction; [notes] section 5: an update
+ * mask keeps fixed reference latents unchanged):
+ *   x[i,:] += coef[s(i)] * v[i,:],   coef[s] = sigma_next - sigma of the
+ *   schedule interval s follows, 0 for the intervals the step leaves alone
+ *   (text, reference images, reference video and audio).
+ *   x, v : [n_tok][dim] contiguous, must not overlap
+ *   coef : host fp32 array, one finite value per interval of segs
+ * Rows whose coefficient is 0 are not touched.  dim a multiple of 8. */
+h3_status h3_euler_update(void* x, const void* v, int64_t n_tok, int32_t dim, const float* coef,
+                          const h3_segment* segs, int32_t n_segs, h3_dtype dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,3 +19,4 @@ from .block import (  # noqa: F401
     rope_inv_freq, rope3d, attention, silu, swiglu, gate_residual,
     block_forward, BRANCH_ATTN, BRANCH_FFN,
 )
+from .stack import shifted_sigma, euler_coefficients, euler_update, stack_forward  # noqa: F401

@@ -169,6 +169,23 @@ def test_attention_validation(lib):
     assert a(q=q + 8) == blk.H3_ERR_ALIGN
 
 
+def test_euler_validation(lib):
+    L = blk.load()
+    segs = blk.segments(CFG1.segments)
+    coef = blk.coefficients([0.0, -0.01, -0.002])
+    def e(x=P, v=P + (1 << 30), n=CFG1.n_tok, dim=CFG1.dim, c=coef, sg=segs, ns=3, dt=blk.H3_F32):
+        return L.h3_euler_update(x, v, n, dim, c, sg, ns, dt, 0)
+    assert e(dt=7) == blk.H3_ERR_DTYPE
+    assert e(x=None) == blk.H3_ERR_ARG
+    assert e(c=None) == blk.H3_ERR_ARG
+    assert e(dim=190) == blk.H3_ERR_SHAPE
+    assert e(v=P + 8) == blk.H3_ERR_ALIGN
+    assert e(v=P + 64) == blk.H3_ERR_ARG                      # v overlaps x
+    assert e(c=blk.coefficients([0.0, float("nan"), 0.0])) == blk.H3_ERR_ARG
+    assert e(ns=2) == blk.H3_ERR_SEGMENTS                     # does not cover the tokens
+    assert e(n=0, ns=0) == blk.H3_OK                          # nothing to do
+
+
 def test_swiglu_and_gate_validation(lib):
     L = blk.load()
     assert L.h3_swiglu(P, P + (1 << 32), 10, 12, 0, 0) == blk.H3_ERR_SHAPE

@@ -21,7 +21,7 @@ H3_BRANCH_ATTN, H3_BRANCH_FFN = 0, 1
 H3_MAX_SEGMENTS = 64
 
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
-           "h3_attention_fwd", "h3_swiglu", "h3_gate_residual")
+           "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update")
 
 
 class H3Segment(ctypes.Structure):
@@ -45,6 +45,7 @@ _SIGS = {
     "h3_attention_fwd": [_P, _P, _P, _I64, _P, _I64, _I64, _I32, _I32, _F, _P, _I32, _P],
     "h3_swiglu": [_P, _P, _I64, _I32, _I32, _P],
     "h3_gate_residual": [_P, _P, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _I32, _P],
+    "h3_euler_update": [_P, _P, _I64, _I32, _P, _P, _I32, _I32, _P],
 }
 
 
@@ -137,3 +138,17 @@ def h3_swiglu(gu, h, n_tok, F, dt, stream=None):
 def h3_gate_residual(x, y, out, n_tok, dim, mod, n_sets, br, segs, n_segs, dt, stream=None):
     _check("h3_gate_residual", load().h3_gate_residual(ptr(x), ptr(y), ptr(out), n_tok, dim, ptr(mod), n_sets, br,
                                                        segs, n_segs, dt, _stream(stream)))
+
+
+def coefficients(values: Iterable[float]) -> "ctypes.Array":
+    """Host fp32 array, one value per interval (h3_euler_update)."""
+    values = list(values)
+    arr = (ctypes.c_float * max(1, len(values)))()
+    for i, v in enumerate(values):
+        arr[i] = float(v)
+    return arr
+
+
+def h3_euler_update(x, v, n_tok, dim, coef, segs, n_segs, dt, stream=None):
+    _check("h3_euler_update", load().h3_euler_update(ptr(x), ptr(v), n_tok, dim, coef, segs, n_segs, dt,
+                                                     _stream(stream)))

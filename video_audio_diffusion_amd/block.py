@@ -52,10 +52,13 @@ class H3Block:
         self.n_segs = len(cfg.segments)
         self.n_sets = int(weights.mod.shape[0])
 
-    def forward(self, x, stream: Optional[int] = None, events=None):
-        """Run the block on x [N, D]; returns the `out` buffer.  With `events`
-        (a list of 12 torch.cuda.Event), event i is recorded before step i."""
-        c, b, w = self.cfg, self.buf, self.w
+    def forward(self, x, stream: Optional[int] = None, events=None, weights: Optional[BlockWeights] = None):
+        """Run the block on x [N, D]; returns the `out` buffer.  x may be the
+        `out` buffer itself (it is read before `out` is written).  `weights`
+        replaces the block's own for this call; with `events` (a list of 12
+        torch.cuda.Event), event i is recorded before step i."""
+        c, b = self.cfg, self.buf
+        w = self.w if weights is None else weights
         N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
         dt, segs, ns, nset = self.dt, self.segs, self.n_segs, self.n_sets
         st = blk.current_stream() if stream is None else stream
@@ -113,3 +116,34 @@ def host_array(t, dtype: str):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
+
+
+class H3Stack:
+    """The backbone of n_blocks blocks and one Euler step of the sampler
+    ([notes] section 3.2: 50 blocks; section 6: one velocity prediction per
+    step).  The blocks share one set of activation buffers; the velocity is
+    the last block's output, and h3_euler_update moves the target intervals
+    of the input latent by the step's coefficients (sampler.py)."""
+
+    def __init__(self, stack_cfg, weights, device="cuda"):
+        from . import sampler
+        self.cfg = stack_cfg
+        self.weights = list(weights)
+        if len(self.weights) != stack_cfg.n_blocks:
+            raise ValueError(f"{len(self.weights)} weight sets for {stack_cfg.n_blocks} blocks")
+        self.block = H3Block(stack_cfg.block, self.weights[0], device)
+        self.coef_values = sampler.step_coefficients(stack_cfg.block.segments, stack_cfg.step,
+                                                     stack_cfg.n_steps, dict(stack_cfg.shifts))
+        self.coef = blk.coefficients(self.coef_values)
+
+    def forward(self, x, stream: Optional[int] = None, block_events=None):
+        """Velocity of latent x [N, D] through every block, then x += coef * v
+        in place; returns x.  With `block_events` (one list of 12 events per
+        block) each block records its per-step events."""
+        c = self.cfg.block
+        st = blk.current_stream() if stream is None else stream
+        h = x
+        for i, w in enumerate(self.weights):
+            h = self.block.forward(h, st, events=None if block_events is None else block_events[i], weights=w)
+        blk.h3_euler_update(x, h, c.n_tok, c.dim, self.coef, self.block.segs, self.block.n_segs, self.block.dt, st)
+        return x

@@ -208,4 +208,25 @@ h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_to
                                            (hipStream_t)stream));
 }
 
+h3_status h3_euler_update(void* x, const void* v, int64_t n_tok, int32_t dim, const float* coef,
+                          const h3_segment* segs, int32_t n_segs, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!x || !v || n_tok < 0 || (n_segs > 0 && !coef)) return H3_ERR_ARG;
+    if (dim < 8 || dim % 8 || n_tok >= kMaxTok) return H3_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(v)) return H3_ERR_ALIGN;
+    const int es = esize(dt);
+    if (overlap(span(x, n_tok, dim, dim, es), span(v, n_tok, dim, dim, es))) return H3_ERR_ARG;
+    SegTable tab;
+    const h3_status st = build_segs(segs, n_segs, n_tok, 0, &tab);
+    if (st != H3_OK) return st;
+    SegCoef c;
+    for (int i = 0; i < kMaxSegs; ++i) c.c[i] = 0.f;
+    for (int i = 0; i < n_segs; ++i) {
+        if (!isfinite(coef[i])) return H3_ERR_ARG;
+        c.c[i] = coef[i];
+    }
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_euler(dt == H3_BF16, x, v, (int32_t)n_tok, dim, tab, c, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -32,6 +32,11 @@ struct SegTable {
     SegDev s[kMaxSegs];
 };
 
+// One fp32 coefficient per interval, passed by value with the table.
+struct SegCoef {
+    float c[kMaxSegs];
+};
+
 __device__ __forceinline__ int find_seg(const SegTable& tab, int32_t i) {
     int k = 0;
     for (int j = 1; j < tab.n; ++j)

@@ -89,6 +89,32 @@ __global__ __launch_bounds__(256) void gate_residual_kernel(const T* x, const T*
 }
 
 // --------------------------------------------------------------------------
+// Euler flow update x += c[interval] * v, one coefficient per interval (zero
+// for the intervals the sampler leaves alone).  Same row mapping as the gate
+// residual: a wavefront per row, 16-byte vectors.
+template <typename T>
+__global__ __launch_bounds__(256) void euler_kernel(T* x, const T* __restrict__ v, int32_t n, int32_t dim,
+                                                    SegTable tab, SegCoef coef) {
+    constexpr int N = Vec<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    const float c = coef.c[find_seg(tab, row)];
+    if (c == 0.f) return;                       // the row stays exactly as it is
+    const int nv = dim / N;
+    char* xr = reinterpret_cast<char*>(x + (int64_t)row * dim);
+    const char* vr = reinterpret_cast<const char*>(v + (int64_t)row * dim);
+    for (int j = lane; j < nv; j += kWave) {
+        float a[N], b[N];
+        Vec<T>::load(xr + 16 * j, a);
+        Vec<T>::load(vr + 16 * j, b);
+#pragma unroll
+        for (int e = 0; e < N; ++e) a[e] = __builtin_fmaf(c, b[e], a[e]);
+        Vec<T>::store(xr + 16 * j, a);
+    }
+}
+
+// --------------------------------------------------------------------------
 // SwiGLU: h = g / (1 + exp(-g)) * u over [gate | up] rows.
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_kernel(const T* __restrict__ gu, T* __restrict__ h,
@@ -203,6 +229,16 @@ hipError_t launch_gate_residual(bool bf, const void* x, const void* y, void* out
     else
         gate_residual_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, (const float*)y,
                                                             (float*)out, n, dim, mod, br, tab);
+    return hipGetLastError();
+}
+
+hipError_t launch_euler(bool bf, void* x, const void* v, int32_t n, int32_t dim, const SegTable& tab,
+                        const SegCoef& coef, hipStream_t st) {
+    const int blocks = (n + 3) / 4;
+    if (bf)
+        euler_kernel<bf16><<<blocks, 256, 0, st>>>((bf16*)x, (const bf16*)v, n, dim, tab, coef);
+    else
+        euler_kernel<float><<<blocks, 256, 0, st>>>((float*)x, (const float*)v, n, dim, tab, coef);
     return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ struct RopeTable {
 hipError_t launch_adaln(bool bf, const void* x, void* y, int32_t n, int32_t dim,
                         const float* mod, int32_t br, const SegTable& tab, float eps,
                         hipStream_t st);
+hipError_t launch_euler(bool bf, void* x, const void* v, int32_t n, int32_t dim, const SegTable& tab,
+                        const SegCoef& coef, hipStream_t st);
 hipError_t launch_gate_residual(bool bf, const void* x, const void* y, void* out, int32_t n,
                                 int32_t dim, const float* mod, int32_t br, const SegTable& tab,
                                 hipStream_t st);

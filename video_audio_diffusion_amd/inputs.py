@@ -144,10 +144,67 @@ CONFIGS: Dict[int, BlockConfig] = {
         segments=pack([("text", MOD_TEXT, 512, 1, 1)]
                       + [(f"ref_image{i}", MOD_VISUAL, 1, 42, 24) for i in range(9)]
                       + [("ref_video", MOD_VISUAL, 90, 42, 24)]
-                      + [(f"audio{i}", MOD_AUDIO, 600, 1, 1) for i in range(4)]
+                      + [(f"ref_audio{i}", MOD_AUDIO, 600, 1, 1) for i in range(3)]
+                      + [("audio", MOD_AUDIO, 600, 1, 1)]
                       + [("video", MOD_VISUAL, 91, 42, 24)]),
         description="Ref2VA-style long sequence, 9:16 15 s target, 194432 tokens"),
 }
+
+
+# ---------------------------------------------------------------- the stack
+
+# Update mask ([notes] section 5): the sampler moves the generation targets
+# (intervals of kind "video" and "audio") and leaves text and reference
+# intervals as they are.  Their schedules' shifts ([notes] section 6: video
+# 12, audio 3).
+TARGET_SHIFTS: Dict[str, float] = {"video": 12.0, "audio": 3.0}
+
+
+@dataclass(frozen=True)
+class StackConfig:
+    """The 50-block backbone ([notes] section 3.2 table) and one Euler step
+    (step `step` of `n_steps`) over the packed sequence of `block`."""
+    name: str
+    block: BlockConfig
+    n_blocks: int = 50
+    n_steps: int = 50
+    step: int = 0
+    shifts: Tuple[Tuple[str, float], ...] = tuple(TARGET_SHIFTS.items())
+    description: str = ""
+
+    @property
+    def n_tok(self) -> int:
+        return self.block.n_tok
+
+
+STACKS: Dict[int, StackConfig] = {
+    5: StackConfig(name="stack50-768p-16x9-15s", block=CONFIGS[3],
+                   description="50 blocks and one Euler step at 92840 tokens"),
+}
+STACK_TINY = StackConfig(name="stack50-tiny-f32", block=CONFIGS[1],
+                         description="50 tiny fp32 blocks and one Euler step (parity)")
+
+
+def stack_seed(cfg_index: int, block: int, tensor: str) -> int:
+    """Seed of one block's tensor in a stack (inside the workload's range of
+    1000 seeds, above the single-block ids)."""
+    return 1000 * cfg_index + 100 + 8 * block + TENSOR_IDS[tensor]
+
+
+def make_stack_block(cfg: BlockConfig, block: int) -> Dict[str, np.ndarray]:
+    """Weights, modulation table and gains of block `block` of a stack."""
+    D, I, F = cfg.dim, cfg.inner, cfg.ffn
+    shapes = {"mod": ((N_MOD_SETS, N_MOD_CHUNKS, D), 1.0), "w_qkv": ((3 * I, D), cfg.w_std),
+              "w_o": ((D, I), cfg.w_std), "w_gu": ((2 * F, D), cfg.w_std), "w_d": ((D, F), cfg.w_std)}
+    out: Dict[str, np.ndarray] = {}
+    for name, (shape, std) in shapes.items():
+        dt = "f32" if name == "mod" else cfg.dtype
+        a = np.empty(shape, dtype=np.uint16 if dt == "bf16" else np.float32)
+        _fill_normal(a, stack_seed(cfg.index, block, name), std, dt)
+        out[name] = a
+    out["gamma_q"] = np.full(cfg.head_dim, cfg.gamma, dtype=np.float32)
+    out["gamma_k"] = np.full(cfg.head_dim, cfg.gamma, dtype=np.float32)
+    return out
 
 
 def permuted(cfg: BlockConfig, order: Sequence[int]) -> Tuple[BlockConfig, np.ndarray]:
