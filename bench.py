@@ -5,14 +5,17 @@ Workload (default): the 15 s 16:9 768p packed sequence -- 512 text tokens,
 600 audio tokens and a 91 x 24 x 42 video grid (92840 tokens) -- through a
 full-width bf16 block (hidden 5376, 56 heads x 128, FFN 14336) with seeded
 synthetic activations and random-init weights.  A step is one block forward:
-the eleven libh3blk calls on one stream, inputs already resident in HBM.
+the eight libh3blk calls of the fused block (the output and down
+projections carry the gated residual, the gate/up projection SwiGLU) on one
+stream, inputs already resident in HBM; --unfused times the eleven-call
+form instead.
 
 Prints one JSON line: block tokens/s (`value`), attention TFLOP/s and % of
 the 2.5 PFLOP/s dense bf16 MFMA peak, per-kernel times, the roofline of the
 dominant kernel (attention) and the fp64 oracle timed on host cores on a
 bounded token sample (`cpu_baseline`).
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3] [--unfused]
 """
 import argparse
 import hashlib
@@ -67,9 +70,13 @@ def step_bytes(cfg):
 
 
 def step_flops(cfg):
+    """Matrix-product flops per launch (a fused epilogue's own arithmetic is
+    not counted)."""
     N, D, H, d, I, F = cfg.n_tok, cfg.dim, cfg.heads, cfg.head_dim, cfg.inner, cfg.ffn
-    return {"gemm_qkv": 2 * N * D * 3 * I, "attention": 4 * N * N * H * d, "gemm_o": 2 * N * I * D,
-            "gemm_gu": 2 * N * D * 2 * F, "gemm_d": 2 * N * F * D}
+    f = {"gemm_qkv": 2 * N * D * 3 * I, "attention": 4 * N * N * H * d, "gemm_o": 2 * N * I * D,
+         "gemm_gu": 2 * N * D * 2 * F, "gemm_d": 2 * N * F * D}
+    f.update(gemm_o_gate=f["gemm_o"], gemm_gu_swiglu=f["gemm_gu"], gemm_d_gate=f["gemm_d"])
+    return f
 
 
 def cpu_baseline(cfg, host, target_s):
@@ -159,6 +166,7 @@ def main():
     ap.add_argument("--config", type=int, default=3,
                     help="workload index: 1-4 one block; 5 the 50-block stack and one Euler step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget; 0 skips it")
+    ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -169,7 +177,7 @@ def main():
     import torch
 
     from video_audio_diffusion_amd import blk, inputs
-    from video_audio_diffusion_amd.block import BlockWeights, H3Block, H3Stack, device_inputs
+    from video_audio_diffusion_amd.block import BlockWeights, H3Block, H3Stack, device_inputs, interleave_gate_up
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -182,7 +190,9 @@ def main():
         log(f"workload {scfg.name}: {scfg.n_blocks} blocks, {cfg.n_tok} tokens; drawing weights on device")
         host = inputs.make_inputs(cfg, ("x",))
         dev = device_inputs(cfg, host)
-        stack = H3Stack(scfg, [device_block_weights(cfg, b) for b in range(scfg.n_blocks)])
+        prep = (lambda w: w) if args.unfused else (lambda w: interleave_gate_up(w, keep_plain=False))
+        stack = H3Stack(scfg, [prep(device_block_weights(cfg, b)) for b in range(scfg.n_blocks)],
+                        fused=not args.unfused)
         log("weights resident on device")
         n_blk = scfg.n_blocks
     else:
@@ -191,21 +201,26 @@ def main():
         host = inputs.make_inputs(cfg)
         dev = device_inputs(cfg, host)
         log("inputs resident on device")
-        block = H3Block(cfg, BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
-                                          dev["gamma_q"], dev["gamma_k"]))
+        w = BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"], dev["gamma_q"],
+                         dev["gamma_k"])
+        if not args.unfused:
+            w = interleave_gate_up(w)
+        block = H3Block(cfg, w, fused=not args.unfused)
         n_blk = 1
     x = dev["x"]
+    steps = (stack.block if stack is not None else block).steps
 
     def one_step(events):
-        """One timed pass: `events` holds 12 events per block and one more
-        recorded after the pass."""
+        """One timed pass: `events` holds len(steps) + 1 events per block and
+        one more recorded after the pass."""
         if stack is None:
             block.forward(x, events=events[0])
         else:
             stack.forward(x, block_events=events)
         events[-1][0].record()
 
-    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(n_blk)] + \
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+                          for _ in range(n_blk)] + \
         [[torch.cuda.Event(enable_timing=True)]]
     for i in range(args.warmup):
         one_step(new_events())
@@ -226,7 +241,7 @@ def main():
 
     # per-kernel time of one pass (summed over the blocks of a stack)
     per = {name: sum(ev[i][b][j].elapsed_time(ev[i][b][j + 1]) for i in range(K) for b in range(n_blk)) / K
-           for j, name in enumerate(H3Block.STEPS)}
+           for j, name in enumerate(steps)}
     flops = {k: v * n_blk for k, v in step_flops(cfg).items()}
     byts = {k: v * n_blk for k, v in step_bytes(cfg).items()}
     peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -252,7 +267,8 @@ def main():
                    "blocks": n_blk, "tokens": cfg.n_tok,
                    "segments": [f"{s.kind} {s.T}x{s.H}x{s.W}" for s in cfg.segments],
                    "hidden": cfg.dim, "heads": cfg.heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
-                   "rope_split": list(cfg.rope_split), "global_batch": 1, "seq_len": cfg.n_tok,
+                   "rope_split": list(cfg.rope_split), "fused_epilogues": not args.unfused,
+                   "global_batch": 1, "seq_len": cfg.n_tok,
                    "parallelism": "none (1 GPU)"},
         "attention_tflops": round(attn_tf, 1), "attention_pct_peak": round(100 * attn_tf / peak_mm, 2),
         "kernels": kernels,

@@ -20,6 +20,10 @@
  *   f   = h3_gemm_bf16(h, W_d)                14336 -> 5376
  *   out = h3_gate_residual(x1, f, FFN)
  *
+ * The fused entry points h3_gemm_gate_residual (output projection + gated
+ * residual) and h3_gemm_swiglu (gate/up projection + SwiGLU) run the same
+ * block in eight calls, without writing y, gu or f to memory.
+ *
  * Conventions shared by every call:
  *   - Tensors are row-major with tokens as rows.  Every pointer argument is
  *     a device pointer unless marked "host".  The caller owns all memory;
@@ -110,6 +114,40 @@ h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim,
 h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw,
                        void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
                        h3_dtype dt, void* stream);
+
+/* The output projection fused with the modality-gated residual ([notes]
+ * section 3: the attention and FFN outputs each re-enter the stream through
+ * the modality's gate and a residual add):
+ *   out[i,:] = x[i,:] + gate[s(i)] * (A . W^T)[i,:],  gate = chunk 3*br+2 of mod,
+ * the same value as h3_gemm_bf16 followed by h3_gate_residual, except that
+ * the product is not rounded to dt before the gate multiplies it.
+ *   A : [M][K] row stride lda;  W : [N][K] row stride ldw
+ *   x, out : [M][N] with row stride ldo; out may equal x (in place), must not
+ *            partially overlap x, and must not overlap A or W
+ *   mod    : fp32 [n_sets][6][N], n_sets >= 1
+ *   segs   : host intervals covering [0, M)
+ * Shape rules of h3_gemm_bf16 apply. */
+h3_status h3_gemm_gate_residual(const void* A, int64_t lda, const void* W, int64_t ldw,
+                                const void* x, void* out, int64_t ldo, int64_t M, int32_t N,
+                                int32_t K, const float* mod, int32_t n_sets, h3_branch br,
+                                const h3_segment* segs, int32_t n_segs, h3_dtype dt,
+                                void* stream);
+
+/* The FFN gate/up projection fused with SwiGLU ([notes] 3.2: the FFN is a
+ * SiLU-gated linear unit of width F):
+ *   H[i,f] = SiLU(a_i . Wg_f) * (a_i . Wu_f),  SiLU(z) = z / (1 + e^-z).
+ *   Wgu : [2F][K] row stride ldw, the gate and up weights interleaved in
+ *         32-row groups: rows 64u..64u+31 are gate rows 32u..32u+31 and rows
+ *         64u+32..64u+63 the up rows 32u..32u+31 (the [gate | up] weight of
+ *         h3_gemm_bf16 with its rows permuted once, when weights are loaded)
+ *   A   : [M][K] row stride lda;  H : [M][F] row stride ldh, must not overlap
+ *         A or Wgu
+ * F a multiple of 32; other shape rules of h3_gemm_bf16 apply.  Equals
+ * h3_gemm_bf16 followed by h3_swiglu except that gate and up are not rounded
+ * to dt before SiLU. */
+h3_status h3_gemm_swiglu(const void* A, int64_t lda, const void* Wgu, int64_t ldw,
+                         void* H, int64_t ldh, int64_t M, int32_t F, int32_t K,
+                         h3_dtype dt, void* stream);
 
 /* Per-head RMSNorm on Q and K ([notes] 3.2: applied per head, before the
  * positional encoding), then 3-D MM-RoPE ([reading] 5 and 7.4), in place:

@@ -204,3 +204,41 @@ def test_valid_arguments_without_a_device_report_hip_error(lib):
     assert _adaln() == blk.H3_ERR_HIP
     L = blk.load()
     assert L.h3_swiglu(P, P + (1 << 32), 10, 64, 0, 0) == blk.H3_ERR_HIP
+
+
+def test_gemm_gate_residual_validation(lib):
+    L = blk.load()
+    segs = blk.segments(CFG1.segments)
+    A, W, x, mod = P, P + (1 << 32), P + (2 << 32), P + (3 << 32)
+    M, N, K = CFG1.n_tok, 192, 128
+
+    def g(A=A, lda=K, W=W, ldw=K, x=x, out=x, ldo=N, M=M, N=N, K=K, mod=mod, ns=3, br=0, sg=segs, nsg=3, dt=0):
+        return L.h3_gemm_gate_residual(A, lda, W, ldw, x, out, ldo, M, N, K, mod, ns, br, sg, nsg, dt, 0)
+    assert g(dt=3) == blk.H3_ERR_DTYPE
+    assert g(x=None) == blk.H3_ERR_ARG
+    assert g(mod=None) == blk.H3_ERR_ARG
+    assert g(br=2) == blk.H3_ERR_ARG
+    assert g(ns=0) == blk.H3_ERR_ARG
+    assert g(ldo=N - 8) == blk.H3_ERR_ARG
+    assert g(K=96, lda=96, ldw=96) == blk.H3_ERR_SHAPE        # bf16 K % 64
+    assert g(x=x + 8) == blk.H3_ERR_ALIGN
+    assert g(out=x + 64) == blk.H3_ERR_ARG                    # out partly overlaps x
+    assert g(out=A) == blk.H3_ERR_ARG                         # out overlaps A
+    assert g(ns=2) == blk.H3_ERR_SEGMENTS                     # an interval uses mod set 2
+    assert g(nsg=2) == blk.H3_ERR_SEGMENTS                    # intervals do not cover M
+    assert g(M=0, sg=None, nsg=0) == blk.H3_OK                # nothing to do
+
+
+def test_gemm_swiglu_validation(lib):
+    L = blk.load()
+    A, W, H = P, P + (1 << 32), P + (2 << 32)
+
+    def s(A=A, lda=5376, W=W, ldw=5376, H=H, ldh=14336, M=100, F=14336, K=5376, dt=0):
+        return L.h3_gemm_swiglu(A, lda, W, ldw, H, ldh, M, F, K, dt, 0)
+    assert s(dt=9) == blk.H3_ERR_DTYPE
+    assert s(F=0) == blk.H3_ERR_ARG
+    assert s(F=14336 - 16) == blk.H3_ERR_SHAPE                # F % 32
+    assert s(ldh=14000) == blk.H3_ERR_ARG
+    assert s(H=A + 64) == blk.H3_ERR_ARG                      # H overlaps A
+    assert s(ldh=14340) == blk.H3_ERR_ALIGN
+    assert s(M=0) == blk.H3_OK

@@ -160,6 +160,36 @@ def test_attention_ragged(n, hd):
     np.testing.assert_allclose(lse.cpu().numpy(), lref, rtol=1e-3, atol=1e-3)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [1, 33, 117, 128, 129, 191, 200])
+def test_attention_after_lds_poison(n, dtype):
+    """Keys past the end get P = 0, so the LDS rows they read must hold no
+    Inf or NaN bits (0 * Inf is NaN), whatever an earlier kernel left there.
+    A GEMM over all-NaN operands first fills every CU's LDS with NaN bit
+    patterns; the short sequences then read ring buffers that no tile of
+    theirs has filled, and ragged tiles."""
+    import torch
+    from video_audio_diffusion_amd.block import device_inputs
+    H, hd = 3, 128
+    I = H * hd
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dt = blk.H3_BF16 if dtype == "bf16" else blk.H3_F32
+    poison = torch.full((4096, 128), float("nan"), dtype=tdt, device="cuda")
+    junk = torch.empty(4096, 4096, dtype=tdt, device="cuda")
+    qkv_h = inputs.draw_rows(None, (n, 3 * I), 300 + n, dtype=dtype)
+    qkv = device_inputs(None, {"qkv": qkv_h})["qkv"]
+    o = torch.empty(n, I, dtype=tdt, device="cuda")
+    blk.h3_gemm_bf16(poison, 128, poison, 128, junk, 4096, 4096, 4096, 128, dt)
+    blk.h3_attention_fwd(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], 3 * I, o, I, n, H, hd, hd ** -0.5, None, dt)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(junk[:8, :8]).all())          # the GEMM did run on NaN operands
+    got = widen(o, dtype)
+    assert np.isfinite(got).all(), f"non-finite attention output at n={n}"
+    f = inputs.widen(qkv_h, dtype)
+    ref = oracle.attention(f[:, :I], f[:, I:2 * I], f[:, 2 * I:], H, hd, hd ** -0.5)
+    assert_close(f"attn after poison n={n} {dtype}", got, ref, TOL[dtype])
+
+
 def test_attention_peaked_full_width():
     """56 heads x 128 over 4097 tokens with logits of std about 16."""
     import torch

@@ -21,7 +21,8 @@ H3_BRANCH_ATTN, H3_BRANCH_FFN = 0, 1
 H3_MAX_SEGMENTS = 64
 
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
-           "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update")
+           "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
+           "h3_gemm_gate_residual", "h3_gemm_swiglu")
 
 
 class H3Segment(ctypes.Structure):
@@ -46,6 +47,9 @@ _SIGS = {
     "h3_swiglu": [_P, _P, _I64, _I32, _I32, _P],
     "h3_gate_residual": [_P, _P, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _I32, _P],
     "h3_euler_update": [_P, _P, _I64, _I32, _P, _P, _I32, _I32, _P],
+    "h3_gemm_gate_residual": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _I32,
+                              _P],
+    "h3_gemm_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P],
 }
 
 
@@ -117,6 +121,31 @@ def h3_adaln_modulate(x, y, n_tok, dim, mod, n_sets, br, segs, n_segs, eps, dt, 
 
 def h3_gemm_bf16(A, lda, W, ldw, C, ldc, M, N, K, dt, stream=None):
     _check("h3_gemm_bf16", load().h3_gemm_bf16(ptr(A), lda, ptr(W), ldw, ptr(C), ldc, M, N, K, dt, _stream(stream)))
+
+
+def h3_gemm_gate_residual(A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets, br, segs, n_segs, dt, stream=None):
+    _check("h3_gemm_gate_residual",
+           load().h3_gemm_gate_residual(ptr(A), lda, ptr(W), ldw, ptr(x), ptr(out), ldo, M, N, K, ptr(mod), n_sets,
+                                        br, segs, n_segs, dt, _stream(stream)))
+
+
+def h3_gemm_swiglu(A, lda, Wgu, ldw, H, ldh, M, F, K, dt, stream=None):
+    _check("h3_gemm_swiglu", load().h3_gemm_swiglu(ptr(A), lda, ptr(Wgu), ldw, ptr(H), ldh, M, F, K, dt,
+                                                   _stream(stream)))
+
+
+def interleave_gate_up_rows(F: int):
+    """Row order that turns a [gate | up] weight of 2F rows into the layout
+    h3_gemm_swiglu reads: 32 gate rows, then the 32 matching up rows, and so
+    on.  Returns the source row of every destination row (a weight-loading
+    permutation, applied once)."""
+    if F % 32:
+        raise ValueError("F must be a multiple of 32")
+    out = []
+    for u in range(F // 32):
+        out.extend(range(32 * u, 32 * u + 32))
+        out.extend(range(F + 32 * u, F + 32 * u + 32))
+    return out
 
 
 def h3_qknorm_rope3d(q, k, ld, n_tok, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base,

@@ -1,4 +1,5 @@
-"""One H3-Omni-Transformer block forward as eleven libh3blk calls.
+"""One H3-Omni-Transformer block forward as eleven libh3blk calls, or as
+eight with the fused projection epilogues.
 
 This driver only allocates device buffers (torch) and issues the calls in
 the block order of the "MiniMax-H3: native audio-video joint generation"
@@ -14,6 +15,9 @@ Buffers (row-major, tokens as rows):
     gu  [N, 2F]   [gate | up]
     h   [N, F]    SwiGLU output
     out [N, D]
+The fused mode writes neither y nor gu: the output and down projections add
+their gated residual in the GEMM epilogue, and the gate/up projection (its
+weight rows interleaved once, `interleave_gate_up`) applies SwiGLU there.
 """
 from __future__ import annotations
 
@@ -32,22 +36,42 @@ class BlockWeights:
     mod: object     # fp32 [n_sets, 6, D]
     gamma_q: object = None   # fp32 [head_dim] or None
     gamma_k: object = None
+    w_gu_il: object = None   # [2F, D] w_gu rows in h3_gemm_swiglu's interleaved order
+
+
+def interleave_gate_up(weights: BlockWeights, keep_plain: bool = True) -> BlockWeights:
+    """Weights with the gate/up rows permuted into the 32-row interleave the
+    fused SwiGLU projection reads (a one-time weight layout step, done with
+    a device gather).  keep_plain=False drops the plain [gate | up] copy."""
+    import dataclasses
+
+    import torch
+    F = weights.w_gu.shape[0] // 2
+    idx = torch.tensor(blk.interleave_gate_up_rows(F), dtype=torch.int64, device=weights.w_gu.device)
+    il = weights.w_gu.index_select(0, idx).contiguous()
+    return dataclasses.replace(weights, w_gu_il=il, w_gu=weights.w_gu if keep_plain else None)
 
 
 class H3Block:
     STEPS = ("adaln_attn", "gemm_qkv", "qknorm_rope", "attention", "gemm_o", "gate_attn",
              "adaln_ffn", "gemm_gu", "swiglu", "gemm_d", "gate_ffn")
+    STEPS_FUSED = ("adaln_attn", "gemm_qkv", "qknorm_rope", "attention", "gemm_o_gate", "adaln_ffn",
+                   "gemm_gu_swiglu", "gemm_d_gate")
 
-    def __init__(self, cfg, weights: BlockWeights, device="cuda"):
+    def __init__(self, cfg, weights: BlockWeights, device="cuda", fused: bool = False):
         import torch
         self.cfg = cfg
         self.w = weights
+        self.fused = fused
+        self.steps = self.STEPS_FUSED if fused else self.STEPS
         self.dt = blk.H3_BF16 if cfg.dtype == "bf16" else blk.H3_F32
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         N, D, I, F = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn
         e = lambda *s: torch.empty(*s, dtype=tdt, device=device)
-        self.buf: Dict[str, object] = {"a": e(N, D), "qkv": e(N, 3 * I), "o": e(N, I), "y": e(N, D),
-                                       "x1": e(N, D), "gu": e(N, 2 * F), "h": e(N, F), "out": e(N, D)}
+        self.buf: Dict[str, object] = {"a": e(N, D), "qkv": e(N, 3 * I), "o": e(N, I), "x1": e(N, D),
+                                       "h": e(N, F), "out": e(N, D)}
+        if not fused:
+            self.buf.update(y=e(N, D), gu=e(N, 2 * F))
         self.segs = blk.segments(cfg.segments)
         self.n_segs = len(cfg.segments)
         self.n_sets = int(weights.mod.shape[0])
@@ -55,10 +79,13 @@ class H3Block:
     def forward(self, x, stream: Optional[int] = None, events=None, weights: Optional[BlockWeights] = None):
         """Run the block on x [N, D]; returns the `out` buffer.  x may be the
         `out` buffer itself (it is read before `out` is written).  `weights`
-        replaces the block's own for this call; with `events` (a list of 12
-        torch.cuda.Event), event i is recorded before step i."""
+        replaces the block's own for this call; with `events` (a list of
+        len(self.steps) + 1 torch.cuda.Event), event i is recorded before
+        step i and the last one after the final step."""
         c, b = self.cfg, self.buf
         w = self.w if weights is None else weights
+        if self.fused:
+            return self._forward_fused(x, stream, events, w)
         N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
         dt, segs, ns, nset = self.dt, self.segs, self.n_segs, self.n_sets
         st = blk.current_stream() if stream is None else stream
@@ -90,6 +117,39 @@ class H3Block:
         rec(10)
         blk.h3_gate_residual(b["x1"], b["y"], b["out"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, dt, st)
         rec(11)
+        return b["out"]
+
+    def _forward_fused(self, x, stream, events, w):
+        if w.w_gu_il is None:
+            raise ValueError("the fused block needs interleaved gate/up weights (interleave_gate_up)")
+        c, b = self.cfg, self.buf
+        N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
+        dt, segs, ns, nset = self.dt, self.segs, self.n_segs, self.n_sets
+        st = blk.current_stream() if stream is None else stream
+        qkv = b["qkv"]
+        q, k, v = qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:]
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+
+        rec(0)
+        blk.h3_adaln_modulate(x, b["a"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, c.eps, dt, st)
+        rec(1)
+        blk.h3_gemm_bf16(b["a"], D, w.w_qkv, D, qkv, 3 * I, N, 3 * I, D, dt, st)
+        rec(2)
+        blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base,
+                             segs, ns, dt, st)
+        rec(3)
+        blk.h3_attention_fwd(q, k, v, 3 * I, b["o"], I, N, H, d, c.scale, None, dt, st)
+        rec(4)
+        blk.h3_gemm_gate_residual(b["o"], I, w.w_o, I, x, b["x1"], D, N, D, I, w.mod, nset, blk.H3_BRANCH_ATTN,
+                                  segs, ns, dt, st)
+        rec(5)
+        blk.h3_adaln_modulate(b["x1"], b["a"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, c.eps, dt, st)
+        rec(6)
+        blk.h3_gemm_swiglu(b["a"], D, w.w_gu_il, D, b["h"], F, N, F, D, dt, st)
+        rec(7)
+        blk.h3_gemm_gate_residual(b["h"], F, w.w_d, F, b["x1"], b["out"], D, N, D, F, w.mod, nset,
+                                  blk.H3_BRANCH_FFN, segs, ns, dt, st)
+        rec(8)
         return b["out"]
 
 
@@ -125,21 +185,22 @@ class H3Stack:
     the last block's output, and h3_euler_update moves the target intervals
     of the input latent by the step's coefficients (sampler.py)."""
 
-    def __init__(self, stack_cfg, weights, device="cuda"):
+    def __init__(self, stack_cfg, weights, device="cuda", fused: bool = False):
         from . import sampler
         self.cfg = stack_cfg
         self.weights = list(weights)
         if len(self.weights) != stack_cfg.n_blocks:
             raise ValueError(f"{len(self.weights)} weight sets for {stack_cfg.n_blocks} blocks")
-        self.block = H3Block(stack_cfg.block, self.weights[0], device)
+        self.block = H3Block(stack_cfg.block, self.weights[0], device, fused=fused)
         self.coef_values = sampler.step_coefficients(stack_cfg.block.segments, stack_cfg.step,
                                                      stack_cfg.n_steps, dict(stack_cfg.shifts))
         self.coef = blk.coefficients(self.coef_values)
 
     def forward(self, x, stream: Optional[int] = None, block_events=None):
         """Velocity of latent x [N, D] through every block, then x += coef * v
-        in place; returns x.  With `block_events` (one list of 12 events per
-        block) each block records its per-step events."""
+        in place; returns x.  With `block_events` (one list of
+        len(self.block.steps) + 1 events per block) each block records its
+        per-step events."""
         c = self.cfg.block
         st = blk.current_stream() if stream is None else stream
         h = x

@@ -56,6 +56,24 @@ h3_status build_segs(const h3_segment* segs, int32_t n_segs, int64_t n_tok, int3
     return H3_OK;
 }
 
+// Shape and layout checks shared by the three GEMM entry points.
+h3_status check_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, const void* C, int64_t ldc,
+                     int64_t M, int32_t N, int32_t K, int32_t Ncols, h3_dtype dt) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!A || !W || !C || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
+    const int es = esize(dt);
+    if (lda < K || ldw < K || ldc < Ncols) return H3_ERR_ARG;
+    if (M >= kMaxTok || N % 8 || K % (dt == H3_BF16 ? 64 : 32)) return H3_ERR_SHAPE;
+    // a 256-row operand tile is addressed with 32-bit byte offsets
+    if (lda * es * 256 >= ((int64_t)1 << 31) || ldw * es * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (lda * es) % 16 || (ldw * es) % 16 ||
+        (ldc * es) % 16)
+        return H3_ERR_ALIGN;
+    const Span c = span(C, M, Ncols, ldc, es);
+    if (overlap(c, span(A, M, K, lda, es)) || overlap(c, span(W, N, K, ldw, es))) return H3_ERR_ARG;
+    return H3_OK;
+}
+
 inline h3_status hip_status(hipError_t e) { return e == hipSuccess ? H3_OK : H3_ERR_HIP; }
 
 }  // namespace
@@ -95,20 +113,39 @@ h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim, 
 
 h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
                        int64_t M, int32_t N, int32_t K, h3_dtype dt, void* stream) {
-    if (!valid_dt(dt)) return H3_ERR_DTYPE;
-    if (!A || !W || !C || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
-    const int es = esize(dt);
-    if (lda < K || ldw < K || ldc < N) return H3_ERR_ARG;
-    if (M >= kMaxTok || N % 8 || K % (dt == H3_BF16 ? 64 : 32)) return H3_ERR_SHAPE;
-    // a 256-row operand tile is addressed with 32-bit byte offsets
-    if (lda * es * 256 >= ((int64_t)1 << 31) || ldw * es * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
-    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (lda * es) % 16 || (ldw * es) % 16 ||
-        (ldc * es) % 16)
-        return H3_ERR_ALIGN;
-    const Span c = span(C, M, N, ldc, es);
-    if (overlap(c, span(A, M, K, lda, es)) || overlap(c, span(W, N, K, ldw, es))) return H3_ERR_ARG;
+    const h3_status st = check_gemm(A, lda, W, ldw, C, ldc, M, N, K, N, dt);
+    if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
     return hip_status(launch_gemm(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, (hipStream_t)stream));
+}
+
+h3_status h3_gemm_gate_residual(const void* A, int64_t lda, const void* W, int64_t ldw, const void* x, void* out,
+                                int64_t ldo, int64_t M, int32_t N, int32_t K, const float* mod, int32_t n_sets,
+                                h3_branch br, const h3_segment* segs, int32_t n_segs, h3_dtype dt,
+                                void* stream) {
+    h3_status st = check_gemm(A, lda, W, ldw, out, ldo, M, N, K, N, dt);
+    if (st != H3_OK) return st;
+    if (!x || !mod || n_sets < 1 || !valid_branch(br)) return H3_ERR_ARG;
+    if (!aligned16(x) || !aligned16(mod)) return H3_ERR_ALIGN;
+    const int es = esize(dt);
+    if (out != x && overlap(span(out, M, N, ldo, es), span(x, M, N, ldo, es))) return H3_ERR_ARG;
+    SegTable tab;
+    st = build_segs(segs, n_segs, M, n_sets, &tab);
+    if (st != H3_OK) return st;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm_gate(dt == H3_BF16, A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets,
+                                       (int32_t)br, tab, (hipStream_t)stream));
+}
+
+h3_status h3_gemm_swiglu(const void* A, int64_t lda, const void* Wgu, int64_t ldw, void* H, int64_t ldh,
+                         int64_t M, int32_t F, int32_t K, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (F < 1 || F > (1 << 29)) return H3_ERR_ARG;
+    if (F % 32) return H3_ERR_SHAPE;
+    const h3_status st = check_gemm(A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, F, dt);
+    if (st != H3_OK) return st;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm_swiglu(dt == H3_BF16, A, lda, Wgu, ldw, H, ldh, M, F, K, (hipStream_t)stream));
 }
 
 h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok, int32_t heads, int32_t head_dim,

@@ -123,6 +123,17 @@ __device__ __forceinline__ void copy_kv_tile2(char* kbuf, char* vbuf, int wave, 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(vbuf + (wave * IPW + i) * 1024), 16, dv[i], 0, 0, 0);
 }
 
+// Clear `bytes` of LDS at p (a multiple of 16) with the workgroup's
+// threads.  The K/V buffers are cleared once, before the first tile copy:
+// keys past the end get P = 0, but 0 times bits left in LDS by an earlier
+// workgroup (Inf or NaN among them) is not 0, and a buffer may be read
+// before any tile has been copied into it (the sweep's padded tail) or
+// hold rows a ragged tile did not fill.  Afterwards every buffer holds
+// zeros or rows of an earlier tile, which are finite.
+__device__ __forceinline__ void zero_lds(char* p, int bytes, int tid) {
+    for (int o = tid * 16; o < bytes; o += kAttnThreads * 16) *reinterpret_cast<u32x4*>(p + o) = (u32x4){};
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ Kp, const T* __restrict__ Vp, int64_t ld,
@@ -308,6 +319,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
     // Retire the Q loads before the key loop: otherwise the wait-count
     // analysis still sees them in flight there and makes the QK products
     // wait for tile copies as well.
+    zero_lds(lds0, 2 * TILE, tid);
+    zero_lds(lds1, 2 * TILE, tid);
+    __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);
     const int ntiles = (n + BKV - 1) / BKV;
     copy_kv_tile<IPW, TILE>(lds0, wave, Kp, Vp, hoff, 0, n, BKV, ld, ldb, dk, dv);
@@ -503,9 +517,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
         }
     };
 
-    // One iteration.  Blocks past the last key are zero-filled by the tile
-    // copies (or stale) and masked to -inf here, so the sweep may run a few
-    // blocks past the end at no cost to the result.  Only the last trips test
+    // One iteration.  Blocks past the last key hold zeros or rows of an
+    // earlier tile (the buffers are cleared before the first copy) and are
+    // masked to -inf here, so the sweep may run a few blocks past the end at
+    // no cost to the result.  Only the last trips test
     // for that (CHECK).
     //
     // Reference: the exponentials of block j are taken against the current
@@ -584,6 +599,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 
     // ---- prologue: tiles 0 and 1 visible, tile 2 in flight; block 0's
     //      logits and V^T, block 1's K
+    zero_lds(k_lds0, TILE, tid);
+    zero_lds(k_lds1, TILE, tid);
+    zero_lds(k_lds2, TILE, tid);
+    zero_lds(v_lds0, TILE, tid);
+    zero_lds(v_lds1, TILE, tid);
+    zero_lds(v_lds2, TILE, tid);
+    __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);
     copy_tile(k_lds0, v_lds0, 0);
     copy_tile(k_lds1, v_lds1, 1);

@@ -25,6 +25,8 @@
 // output: their A and W panels are then shared in that XCD's L2.
 #include "launch.h"
 
+#include <type_traits>
+
 namespace h3 {
 
 template <typename T> struct GemmMfma;
@@ -36,6 +38,7 @@ template <> struct GemmMfma<bf16> {
                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     }
     __device__ __forceinline__ static void store(bf16* p, float v) { *p = (bf16)v; }
+    __device__ __forceinline__ static float load(const bf16* p) { return (float)*p; }
 };
 
 template <> struct GemmMfma<float> {
@@ -48,6 +51,7 @@ template <> struct GemmMfma<float> {
                                                        0, 0, 0);
     }
     __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
 };
 
 constexpr int kBM = 256, kBN = 256;
@@ -84,11 +88,28 @@ __device__ __forceinline__ void copy_operand(char* lds, int wave, const void* ba
                                                  0);
 }
 
-template <typename T, int ROWB, int STAGES, int NWAVES>
+// Epilogues.  EpiStore writes C.  EpiGate writes out = x + gate * C with
+// the modality gate of each row's interval (the block's gated residual, so
+// the projection output never goes to memory).  EpiSwiglu takes W with its
+// rows interleaved in 64-row units -- rows 64u..64u+31 the gate rows
+// 32u..32u+31, rows 64u+32..64u+63 the matching up rows -- so every
+// wavefront's two 32-column blocks hold a gate column and its up column in
+// the same lanes, and writes h = SiLU(gate) * up at half the width.
+struct EpiStore {};
+struct EpiGate {
+    const void* x;          // [M][N], row stride ldc (may equal C)
+    const float* mod;       // [n_sets][6][N]
+    int32_t chunk;          // gate chunk index 3 * branch + 2
+    SegTable tab;
+};
+struct EpiSwiglu {};
+
+template <typename T, int ROWB, int STAGES, int NWAVES, typename EPI>
 __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__ A, int64_t lda,
                                                    const T* __restrict__ W, int64_t ldw,
                                                    T* __restrict__ C, int64_t ldc, int32_t M, int32_t N,
-                                                   int32_t K, int32_t tiles_m, int32_t tiles_n, int32_t group_m) {
+                                                   int32_t K, int32_t tiles_m, int32_t tiles_n, int32_t group_m,
+                                                   EPI epi) {
     using Geo = GemmGeom<ROWB, STAGES, NWAVES>;
     constexpr int NJ = Geo::NJ;
     constexpr int ES = sizeof(T);
@@ -221,30 +242,115 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
 
     // ---- epilogue: accumulator (lane, r) -> row 8(r/4) + 4(lane/32) + r%4, col lane%32
     const bool full = m0 + kBM <= M && n0 + kBN <= N;
-    T* cbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
-    if (full) {
+    if constexpr (std::is_same<EPI, EpiStore>::value) {
+        T* cbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
+                                           acc[i][j][r]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int col = n0 + wn * NJ * 32 + j * 32 + frow;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                        if (row < M && col < N)
+                            GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
+                                               acc[i][j][r]);
+                    }
+                }
+        }
+    } else if constexpr (std::is_same<EPI, EpiGate>::value) {
+        const T* xb = reinterpret_cast<const T*>(epi.x);
+        // One interval usually covers the whole tile: then every row takes the
+        // same modality set; otherwise each row looks its interval up.
+        const int last = (m0 + kBM < M ? m0 + kBM : M) - 1;
+        const int seg0 = find_seg(epi.tab, m0);
+        const bool one_set = seg0 == find_seg(epi.tab, last);
+        const int set0 = epi.tab.s[seg0].mod_set;
+        // gates of this lane's columns: loaded once for a one-set tile, per row
+        // (from cache) on the few tiles an interval boundary crosses
+        const float* gbase = epi.mod + (int64_t)epi.chunk * N + n0 + wn * NJ * 32 + frow;
+        const int64_t set_stride = (int64_t)6 * N;
+        float g0[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            g0[j] = n0 + wn * NJ * 32 + j * 32 + frow < N ? gbase[set0 * set_stride + j * 32] : 0.f;
+        auto gate = [&](int row, int j) __attribute__((always_inline)) {
+            return one_set ? g0[j] : gbase[epi.tab.s[find_seg(epi.tab, row)].mod_set * set_stride + j * 32];
+        };
+        const int64_t obase = (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
+        if (full) {
+            // per 32-row block: all 16 x NJ residual loads first, then the stores
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float xv[16][NJ];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
-                                       acc[i][j][r]);
-    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int col = n0 + wn * NJ * 32 + j * 32 + frow;
+                    for (int j = 0; j < NJ; ++j)
+                        xv[r][j] = GemmMfma<T>::load(xb + obase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc +
+                                                     j * 32);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                    if (row < M && col < N)
-                        GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
-                                           acc[i][j][r]);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        GemmMfma<T>::store(C + obase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
+                                           xv[r][j] + gate(row, j) * acc[i][j][r]);
                 }
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    if (row >= M) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int col = n0 + wn * NJ * 32 + j * 32 + frow;
+                        if (col >= N) continue;
+                        const int64_t o = (int64_t)row * ldc + col;
+                        GemmMfma<T>::store(C + o, GemmMfma<T>::load(xb + o) + gate(row, j) * acc[i][j][r]);
+                    }
+                }
+        }
+    } else {
+        static_assert(std::is_same<EPI, EpiSwiglu>::value && NJ == 2, "SwiGLU pairs a wavefront's two blocks");
+        // output column of this lane: half the interleaved column index
+        const int hcol = (n0 >> 1) + wn * 32 + frow;
+        const int F = N >> 1;
+        auto hval = [&](float gt, float up) __attribute__((always_inline)) {
+            return gt / (1.0f + __expf(-gt)) * up;
+        };
+        T* hbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + hcol;
+        if (full) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
+                                       hval(acc[i][0][r], acc[i][1][r]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    if (row < M && hcol < F)
+                        GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
+                                           hval(acc[i][0][r], acc[i][1][r]));
+                }
+        }
     }
 }
 
@@ -265,20 +371,42 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
 #define H3_GEMM_WAVES 8
 #endif
 
-hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
-                       int64_t ldc, int64_t M, int32_t N, int32_t K, hipStream_t st) {
+template <typename EPI>
+hipError_t launch_gemm_epi(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+                           int64_t M, int32_t N, int32_t K, const EPI& epi, hipStream_t st) {
     const int tiles_m = (int)((M + kBM - 1) / kBM);
     const int tiles_n = (N + kBN - 1) / kBN;
     const int grid = tiles_m * tiles_n;
     if (bf)
-        gemm_kernel<bf16, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
+        gemm_kernel<bf16, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
             (const bf16*)A, lda, (const bf16*)W, ldw, (bf16*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-            H3_GEMM_GROUP_M);
+            H3_GEMM_GROUP_M, epi);
     else
-        gemm_kernel<float, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
+        gemm_kernel<float, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
             (const float*)A, lda, (const float*)W, ldw, (float*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-            H3_GEMM_GROUP_M);
+            H3_GEMM_GROUP_M, epi);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                       int64_t ldc, int64_t M, int32_t N, int32_t K, hipStream_t st) {
+    return launch_gemm_epi(bf, A, lda, W, ldw, C, ldc, M, N, K, EpiStore{}, st);
+}
+
+hipError_t launch_gemm_gate(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, const void* x,
+                            void* out, int64_t ldo, int64_t M, int32_t N, int32_t K, const float* mod,
+                            int32_t n_sets, int32_t br, const SegTable& tab, hipStream_t st) {
+    EpiGate e;
+    e.x = x;
+    e.mod = mod;
+    e.chunk = 3 * br + 2;
+    e.tab = tab;
+    return launch_gemm_epi(bf, A, lda, W, ldw, out, ldo, M, N, K, e, st);
+}
+
+hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* Wgu, int64_t ldw, void* H,
+                              int64_t ldh, int64_t M, int32_t F, int32_t K, hipStream_t st) {
+    return launch_gemm_epi(bf, A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, EpiSwiglu{}, st);
 }
 
 }  // namespace h3

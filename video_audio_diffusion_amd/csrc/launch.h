@@ -25,6 +25,11 @@ hipError_t launch_swiglu(bool bf, const void* gu, void* h, int64_t n, int32_t F,
 hipError_t launch_qknorm_rope(bool bf, void* q, void* k, int64_t ld, int32_t n, int32_t heads,
                               int32_t hd, const float* gq, const float* gk, float eps,
                               const RopeTable& rt, const SegTable& tab, hipStream_t st);
+hipError_t launch_gemm_gate(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, const void* x,
+                            void* out, int64_t ldo, int64_t M, int32_t N, int32_t K, const float* mod,
+                            int32_t n_sets, int32_t br, const SegTable& tab, hipStream_t st);
+hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* Wgu, int64_t ldw, void* H,
+                              int64_t ldh, int64_t M, int32_t F, int32_t K, hipStream_t st);
 hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                        int64_t ldc, int64_t M, int32_t N, int32_t K, hipStream_t st);
 hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v, int64_t ld_qkv,
