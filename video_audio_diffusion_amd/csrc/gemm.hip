@@ -231,9 +231,17 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
                 // counter holds 15)
                 wait_vm<63, true>();
                 read_chunk(ks, kk + 1, fa[(kk + 1) & 1], fw[(kk + 1) & 1]);
-            } else if (ks + 1 < nk) {
-                step_ready(ks + 1, nk);
-                read_chunk(ks + 1, 0, fa[0], fw[0]);
+            } else {
+                // This chunk's fragments (read a chunk of MFMAs ago) land
+                // here on every path, so the MFMAs below never wait for the
+                // next step's reads issued after the barrier; without it the
+                // compiler merges the last step's counter state into the
+                // common path and stalls every step on those fresh reads.
+                wait_vm<63, true>();
+                if (ks + 1 < nk) {
+                    step_ready(ks + 1, nk);
+                    read_chunk(ks + 1, 0, fa[0], fw[0]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);   // the reads above go out before these MFMAs
             mfma_chunk(fa[kk & 1], fw[kk & 1]);
