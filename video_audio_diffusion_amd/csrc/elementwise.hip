@@ -139,7 +139,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const T* __restrict__ gu, T
 // --------------------------------------------------------------------------
 // Per-head RMSNorm of Q and K, then 3-D MM-RoPE, in place.  One workgroup
 // per token: the token's (cos, sin) per pair are computed once into LDS and
-// reused by all 2*heads head vectors; LPH lanes share one head vector.
+// reused by all 2*heads head vectors; LPH lanes share one head vector.  A
+// thread's head vectors are handled QR at a time with every load issued
+// before any is used (the pass is bound by how many bytes are in flight),
+// and the first batch's loads go out before the (cos, sin) computation.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* q, T* k, int64_t ld, int32_t n,
                                                           int32_t heads,
@@ -149,9 +152,33 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* q, T* k, int64_t ld
     constexpr int N = Vec<T>::N;
     constexpr int LPH = HD / N;           // lanes per head vector
     constexpr int GROUPS = 256 / LPH;     // head vectors per round
+    constexpr int QR = 4;                 // rounds whose loads are in flight together
     __shared__ f32x2 cs[HD / 2];
     const int row = blockIdx.x;
     if (row >= n) return;                 // uniform for the workgroup
+    const int sub = threadIdx.x % LPH;
+    const int grp = threadIdx.x / LPH;
+    const int nhv = 2 * heads;
+    auto vec_ptr = [&](int hv) __attribute__((always_inline)) -> T* {
+        const bool isq = hv < heads;
+        return (isq ? q : k) + (int64_t)row * ld + (int64_t)(isq ? hv : hv - heads) * HD + sub * N;
+    };
+    float v[QR][N];
+    auto load_batch = [&](int hv0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < QR; ++u) {
+            const int hv = hv0 + u * GROUPS;
+            if (hv < nhv) Vec<T>::load(vec_ptr(hv), v[u]);
+        }
+    };
+    load_batch(grp);
+    // this thread's N gains for q and for k, loaded once (1 when absent)
+    float gqv[N], gkv[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        gqv[e] = gq ? gq[sub * N + e] : 1.0f;
+        gkv[e] = gk ? gk[sub * N + e] : 1.0f;
+    }
     if (threadIdx.x < HD / 2) {
         const int p = threadIdx.x;
         const int s = find_seg(tab, row);
@@ -165,29 +192,31 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* q, T* k, int64_t ld
         cs[p] = (f32x2){(float)c, (float)sn};
     }
     __syncthreads();
-    const int sub = threadIdx.x % LPH;
-    const int grp = threadIdx.x / LPH;
-    for (int hv = grp; hv < 2 * heads; hv += GROUPS) {
-        const bool isq = hv < heads;
-        T* base = (isq ? q : k) + (int64_t)row * ld + (int64_t)(isq ? hv : hv - heads) * HD + sub * N;
-        const float* gamma = isq ? gq : gk;
-        float v[N];
-        Vec<T>::load(base, v);
-        float ss = 0.f;
+    for (int hv0 = grp; hv0 < nhv; hv0 += QR * GROUPS) {
+        if (hv0 != grp) load_batch(hv0);
 #pragma unroll
-        for (int e = 0; e < N; ++e) ss += v[e] * v[e];
-        ss = sum_lanes<LPH>(ss);
-        const float rstd = 1.0f / __builtin_sqrtf(ss / (float)HD + eps);
+        for (int u = 0; u < QR; ++u) {
+            const int hv = hv0 + u * GROUPS;
+            // hv < nhv is uniform across a head vector's LPH lanes (the
+            // lane-sum below stays among them)
+            if (hv >= nhv) break;
+            const bool isq = hv < heads;
+            float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < N; ++e) v[e] *= rstd * (gamma ? gamma[sub * N + e] : 1.0f);
+            for (int e = 0; e < N; ++e) ss += v[u][e] * v[u][e];
+            ss = sum_lanes<LPH>(ss);
+            const float rstd = 1.0f / __builtin_sqrtf(ss / (float)HD + eps);
 #pragma unroll
-        for (int e = 0; e < N; e += 2) {
-            const f32x2 t = cs[(sub * N + e) / 2];
-            const float u0 = v[e], u1 = v[e + 1];
-            v[e] = u0 * t.x - u1 * t.y;
-            v[e + 1] = u0 * t.y + u1 * t.x;
+            for (int e = 0; e < N; ++e) v[u][e] *= rstd * (isq ? gqv[e] : gkv[e]);
+#pragma unroll
+            for (int e = 0; e < N; e += 2) {
+                const f32x2 t = cs[(sub * N + e) / 2];
+                const float u0 = v[u][e], u1 = v[u][e + 1];
+                v[u][e] = u0 * t.x - u1 * t.y;
+                v[u][e + 1] = u0 * t.y + u1 * t.x;
+            }
+            Vec<T>::store(vec_ptr(hv), v[u]);
         }
-        Vec<T>::store(base, v);
     }
 }
 
