@@ -20,3 +20,4 @@ from .block import (  # noqa: F401
     block_forward, BRANCH_ATTN, BRANCH_FFN,
 )
 from .stack import shifted_sigma, euler_coefficients, euler_update, stack_forward  # noqa: F401
+from .io import patchify, unpatchify, project_inputs, project_outputs  # noqa: F401
