@@ -158,6 +158,79 @@ def device_block_weights(cfg, b):
                         rnd("mod", (inputs.N_MOD_SETS, inputs.N_MOD_CHUNKS, D), 1.0, torch.float32), gain, gain)
 
 
+def bench_adapters(args):
+    """The input and output adapters around the backbone at one workload:
+    patchify and input projection of every interval into the packed
+    sequence, then output projection and unpatchify of the targets."""
+    import torch
+
+    from video_audio_diffusion_amd import adapters, inputs
+    from video_audio_diffusion_amd.block import device_inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    acfg = adapters.AdapterConfig(block=cfg, text_width=64 if cfg.dtype == "f32" else 5120)
+    log(f"adapters of {cfg.name}: {cfg.n_tok} tokens; drawing inputs")
+    host = inputs.make_adapter_inputs(cfg, acfg.text_width)
+    dev = device_inputs(cfg, host)
+    w = adapters.AdapterWeights({m: adapters.pad_columns(dev["w_in/" + m], acfg.k_pad(m)) for m in ("text", "video", "audio")},
+                                {m: dev["w_out/" + m] for m in ("video", "audio")})
+    ad = adapters.H3Adapters(acfg, w)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    feats = {s.kind: dev["feat/" + s.kind] for s in cfg.segments}
+    x = torch.empty(cfg.n_tok, cfg.dim, dtype=tdt, device="cuda")
+    shapes = inputs.adapter_shapes(cfg, acfg.text_width)
+    lat_out = {k: torch.empty(shapes["feat/" + k], dtype=tdt, device="cuda") for k in adapters.TARGET_KINDS}
+
+    def one(marks):
+        mark = (lambda name: marks.append((name, torch.cuda.Event(enable_timing=True)))) if marks is not None else None
+        rec = (lambda name: (mark(name), marks[-1][1].record())) if marks is not None else None
+        ad.pack(feats, x, mark=rec)
+        ad.unpack(x, lat_out, mark=rec)
+        if marks is not None:
+            rec("end")
+
+    for i in range(args.warmup):
+        one(None)
+    torch.cuda.synchronize()
+    K = args.steps
+    runs = [[] for _ in range(K)]
+    for i in range(K):
+        one(runs[i])
+    torch.cuda.synchronize()
+    total_ms = runs[0][0][1].elapsed_time(runs[-1][-1][1]) / K
+    e = 2 if cfg.dtype == "bf16" else 4
+    names = [n for n, _ in runs[0][:-1]]
+    per = {n: sum(r[j][1].elapsed_time(r[j + 1][1]) for r in runs) / K for j, n in enumerate(names)}
+    kern = {}
+    for s in cfg.segments:
+        m = inputs.modality(s.kind)
+        kp, P = acfg.k_pad(m), acfg.feature_width(m)
+        if ("patchify_" + s.kind) in per:
+            by = s.length * P * e + s.length * kp * e
+            kern["patchify_" + s.kind] = {"ms": round(per["patchify_" + s.kind], 4),
+                                          "gbs": round(by / (per["patchify_" + s.kind] * 1e-3) / 1e9, 1)}
+        fl = 2 * s.length * cfg.dim * kp
+        kern["gemm_in_" + s.kind] = {"ms": round(per["gemm_in_" + s.kind], 4),
+                                     "tflops": round(fl / (per["gemm_in_" + s.kind] * 1e-3) / 1e12, 1)}
+        if s.kind in adapters.TARGET_KINDS:
+            fl = 2 * s.length * cfg.dim * P
+            kern["gemm_out_" + s.kind] = {"ms": round(per["gemm_out_" + s.kind], 4),
+                                          "tflops": round(fl / (per["gemm_out_" + s.kind] * 1e-3) / 1e12, 1)}
+            if ("unpatchify_" + s.kind) in per:
+                by = 2 * s.length * P * e
+                kern["unpatchify_" + s.kind] = {"ms": round(per["unpatchify_" + s.kind], 4),
+                                                "gbs": round(by / (per["unpatchify_" + s.kind] * 1e-3) / 1e9, 1)}
+    result = {"metric": "H3 I/O adapters (patchify, input/output projections, unpatchify) tokens/s",
+              "value": round(cfg.n_tok / (total_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+              "warmup": args.warmup, "ms_per_step": round(total_ms, 4), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+              "config": {"workload": f"{cfg.name} adapters", "tokens": cfg.n_tok, "hidden": cfg.dim,
+                         "text_width": acfg.text_width, "video_patch": list(acfg.video_patch),
+                         "segments": [f"{s.kind} {s.T}x{s.H}x{s.W}" for s in cfg.segments]},
+              "kernels": kern}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +240,8 @@ def main():
                     help="workload index: 1-4 one block; 5 the 50-block stack and one Euler step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget; 0 skips it")
     ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
+    ap.add_argument("--io", action="store_true",
+                    help="time the input/output adapters (patchify, projections, unpatchify) of the workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -183,6 +258,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     blk.load()
+    if args.io:
+        bench_adapters(args)
+        return
     stack = None
     if args.config in inputs.STACKS:
         scfg = inputs.STACKS[args.config]

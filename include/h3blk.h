@@ -211,6 +211,32 @@ h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_to
 h3_status h3_euler_update(void* x, const void* v, int64_t n_tok, int32_t dim, const float* coef,
                           const h3_segment* segs, int32_t n_segs, h3_dtype dt, void* stream);
 
+/* Patchify of a latent for the backbone's input projection ([notes] 4.1: the
+ * 24-channel visual latent is cut into 1x2x2 patches over (t, h, w), 96
+ * values each; [reading] 7.3: the patch grid is then flattened with t
+ * slowest and w fastest; [notes] 4.3: an audio token carries 32 latent
+ * channels, i.e. a 1x1x1 patch):
+ *   tokens[i, f] = latent[t*pt + dt, h*ph + dh, w*pw + dw, c],
+ *   i = (t * H/ph + h) * W/pw + w,   f = ((dt*ph + dh)*pw + dw)*C + c,
+ * and tokens[i, f] = 0 for pt*ph*pw*C <= f < ld, so a token row can feed
+ * h3_gemm_bf16 with K = ld (zero features times zero weight columns).
+ *   latent : [T][H][W][C] contiguous, channels last
+ *   tokens : [(T/pt)(H/ph)(W/pw)][ld] row-major; must not overlap latent
+ * T, H, W multiples of pt, ph, pw; C a multiple of 8 (bf16) or 4 (fp32);
+ * ld >= pt*ph*pw*C and a multiple of 8 (bf16) or 4 (fp32); T == 0 is a
+ * no-op.  Bits are copied, never rounded. */
+h3_status h3_patchify(const void* latent, int32_t T, int32_t H, int32_t W, int32_t C,
+                      int32_t pt, int32_t ph, int32_t pw, void* tokens, int64_t ld,
+                      h3_dtype dt, void* stream);
+
+/* Inverse of h3_patchify for the output projection ([notes] 2.3: the
+ * backbone predicts the update of the video and audio latents): columns
+ * f < pt*ph*pw*C of every token row go back to their latent positions;
+ * columns at or past that are not read.  Same argument rules. */
+h3_status h3_unpatchify(const void* tokens, int64_t ld, int32_t T, int32_t H, int32_t W,
+                        int32_t C, int32_t pt, int32_t ph, int32_t pw, void* latent,
+                        h3_dtype dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -242,3 +242,25 @@ def test_gemm_swiglu_validation(lib):
     assert s(H=A + 64) == blk.H3_ERR_ARG                      # H overlaps A
     assert s(ldh=14340) == blk.H3_ERR_ALIGN
     assert s(M=0) == blk.H3_OK
+
+
+def test_patchify_validation(lib):
+    L = blk.load()
+    lat, tok = P, P + (1 << 32)
+
+    def pf(lat=lat, T=91, H=48, W=84, C=24, pt=1, ph=2, pw=2, tok=tok, ld=128, dt=0):
+        return L.h3_patchify(lat, T, H, W, C, pt, ph, pw, tok, ld, dt, 0)
+
+    def uf(lat=lat, T=91, H=48, W=84, C=24, pt=1, ph=2, pw=2, tok=tok, ld=128, dt=0):
+        return L.h3_unpatchify(tok, ld, T, H, W, C, pt, ph, pw, lat, dt, 0)
+    for f in (pf, uf):
+        assert f(dt=5) == blk.H3_ERR_DTYPE
+        assert f(lat=None) == blk.H3_ERR_ARG
+        assert f(ph=0) == blk.H3_ERR_ARG
+        assert f(H=47) == blk.H3_ERR_SHAPE                    # not a multiple of the patch
+        assert f(C=20) == blk.H3_ERR_SHAPE                    # bf16 channels in 16-byte vectors
+        assert f(ld=88) == blk.H3_ERR_ARG                     # row narrower than a patch (96)
+        assert f(ld=100) == blk.H3_ERR_ALIGN
+        assert f(tok=lat + 64) == blk.H3_ERR_ARG              # overlaps the latent
+        assert f(T=0) == blk.H3_OK                            # nothing to do
+    assert pf(C=20, dt=1, ld=80) != blk.H3_ERR_SHAPE          # fp32: 4-element vectors

@@ -22,7 +22,7 @@ H3_MAX_SEGMENTS = 64
 
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
-           "h3_gemm_gate_residual", "h3_gemm_swiglu")
+           "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify")
 
 
 class H3Segment(ctypes.Structure):
@@ -50,6 +50,8 @@ _SIGS = {
     "h3_gemm_gate_residual": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _I32,
                               _P],
     "h3_gemm_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P],
+    "h3_patchify": [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P],
+    "h3_unpatchify": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P],
 }
 
 
@@ -132,6 +134,16 @@ def h3_gemm_gate_residual(A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets, br,
 def h3_gemm_swiglu(A, lda, Wgu, ldw, H, ldh, M, F, K, dt, stream=None):
     _check("h3_gemm_swiglu", load().h3_gemm_swiglu(ptr(A), lda, ptr(Wgu), ldw, ptr(H), ldh, M, F, K, dt,
                                                    _stream(stream)))
+
+
+def h3_patchify(latent, T, H, W, C, pt, ph, pw, tokens, ld, dt, stream=None):
+    _check("h3_patchify", load().h3_patchify(ptr(latent), T, H, W, C, pt, ph, pw, ptr(tokens), ld, dt,
+                                             _stream(stream)))
+
+
+def h3_unpatchify(tokens, ld, T, H, W, C, pt, ph, pw, latent, dt, stream=None):
+    _check("h3_unpatchify", load().h3_unpatchify(ptr(tokens), ld, T, H, W, C, pt, ph, pw, ptr(latent), dt,
+                                                 _stream(stream)))
 
 
 def interleave_gate_up_rows(F: int):

@@ -266,4 +266,44 @@ h3_status h3_euler_update(void* x, const void* v, int64_t n_tok, int32_t dim, co
     return hip_status(launch_euler(dt == H3_BF16, x, v, (int32_t)n_tok, dim, tab, c, (hipStream_t)stream));
 }
 
+// Shared checks of the patch calls: grid and patch sizes, the vector width,
+// the row stride, alignment and overlap.  Writes the token count to *n_tok.
+static h3_status check_patch(const void* lat, const void* tok, int64_t ld, int32_t T, int32_t H, int32_t W,
+                             int32_t C, int32_t pt, int32_t ph, int32_t pw, h3_dtype dt, int64_t* n_tok) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!lat || !tok || T < 0 || H < 1 || W < 1 || C < 1 || pt < 1 || ph < 1 || pw < 1) return H3_ERR_ARG;
+    if (T % pt || H % ph || W % pw) return H3_ERR_SHAPE;
+    const int es = esize(dt), vec = 16 / es;
+    if (C % vec) return H3_ERR_SHAPE;
+    const int64_t P = (int64_t)pt * ph * pw * C;
+    if (P >= (1 << 30) || (int64_t)H * W * C >= ((int64_t)1 << 40)) return H3_ERR_SHAPE;
+    if (ld < P) return H3_ERR_ARG;
+    if (ld % vec || !aligned16(lat) || !aligned16(tok)) return H3_ERR_ALIGN;
+    const int64_t n = (int64_t)(T / pt) * (H / ph) * (W / pw);
+    if (n >= kMaxTok) return H3_ERR_SHAPE;
+    if (overlap(span(lat, 1, (int64_t)T * H * W * C, 0, es), span(tok, n, ld, ld, es))) return H3_ERR_ARG;
+    *n_tok = n;
+    return H3_OK;
+}
+
+h3_status h3_patchify(const void* latent, int32_t T, int32_t H, int32_t W, int32_t C, int32_t pt, int32_t ph,
+                      int32_t pw, void* tokens, int64_t ld, h3_dtype dt, void* stream) {
+    int64_t n = 0;
+    const h3_status st = check_patch(latent, tokens, ld, T, H, W, C, pt, ph, pw, dt, &n);
+    if (st != H3_OK) return st;
+    if (n == 0) return H3_OK;
+    return hip_status(launch_patchify(dt == H3_BF16, latent, tokens, ld, PatchGeom{T, H, W, C, pt, ph, pw}, n,
+                                      (hipStream_t)stream));
+}
+
+h3_status h3_unpatchify(const void* tokens, int64_t ld, int32_t T, int32_t H, int32_t W, int32_t C, int32_t pt,
+                        int32_t ph, int32_t pw, void* latent, h3_dtype dt, void* stream) {
+    int64_t n = 0;
+    const h3_status st = check_patch(latent, tokens, ld, T, H, W, C, pt, ph, pw, dt, &n);
+    if (st != H3_OK) return st;
+    if (n == 0) return H3_OK;
+    return hip_status(launch_unpatchify(dt == H3_BF16, tokens, ld, latent, PatchGeom{T, H, W, C, pt, ph, pw},
+                                        (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -221,6 +221,86 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* q, T* k, int64_t ld
 }
 
 // --------------------------------------------------------------------------
+// Patchify / unpatchify of a channels-last latent [T][H][W][C] with a
+// (pt, ph, pw) patch.  Token i = (t * Hp + h) * Wp + w (w fastest) holds its
+// patch's values in (dt, dh, dw, c) order, then zeros up to the row stride
+// ld, so a token row can feed a GEMM whose K is ld.  One thread per 16-byte
+// vector: C is a multiple of the vector width, so a vector never leaves one
+// latent position.  Pure data movement: bits are copied, never rounded.
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const T* __restrict__ lat, T* __restrict__ tok, int64_t ld,
+                                                       PatchGeom g, int64_t n_tok) {
+    constexpr int V = Vec<T>::N;
+    const int Hp = g.H / g.ph, Wp = g.W / g.pw;
+    const int P = g.pt * g.ph * g.pw * g.C;
+    const int64_t vpr = ld / V;
+    const int64_t total = n_tok * vpr;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx / vpr;
+        const int f = (int)(idx - i * vpr) * V;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (f < P) {
+            const int c = f % g.C;
+            int q = f / g.C;
+            const int dw = q % g.pw;
+            q /= g.pw;
+            const int dh = q % g.ph, dt = q / g.ph;
+            const int w = (int)(i % Wp);
+            const int64_t r = i / Wp;
+            const int h = (int)(r % Hp), t = (int)(r / Hp);
+            const int64_t src =
+                (((int64_t)(t * g.pt + dt) * g.H + h * g.ph + dh) * g.W + w * g.pw + dw) * g.C + c;
+            val = *reinterpret_cast<const u32x4*>(lat + src);
+        }
+        *reinterpret_cast<u32x4*>(tok + i * ld + f) = val;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void unpatchify_kernel(const T* __restrict__ tok, int64_t ld,
+                                                         T* __restrict__ lat, PatchGeom g, int64_t n_vec) {
+    constexpr int V = Vec<T>::N;
+    const int Hp = g.H / g.ph, Wp = g.W / g.pw;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_vec;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = idx * V;
+        const int c = (int)(e % g.C);
+        int64_t pos = e / g.C;
+        const int wl = (int)(pos % g.W);
+        pos /= g.W;
+        const int hl = (int)(pos % g.H), tl = (int)(pos / g.H);
+        const int64_t i = ((int64_t)(tl / g.pt) * Hp + hl / g.ph) * Wp + wl / g.pw;
+        const int f = (((tl % g.pt) * g.ph + hl % g.ph) * g.pw + wl % g.pw) * g.C + c;
+        *reinterpret_cast<u32x4*>(lat + e) = *reinterpret_cast<const u32x4*>(tok + i * ld + f);
+    }
+}
+
+static int stream_blocks(int64_t work) {
+    const int64_t b = (work + 255) / 256;
+    return (int)(b < 8192 ? (b < 1 ? 1 : b) : 8192);
+}
+
+hipError_t launch_patchify(bool bf, const void* lat, void* tok, int64_t ld, const PatchGeom& g, int64_t n_tok,
+                           hipStream_t st) {
+    const int64_t work = n_tok * (ld / (bf ? 8 : 4));
+    if (bf)
+        patchify_kernel<bf16><<<stream_blocks(work), 256, 0, st>>>((const bf16*)lat, (bf16*)tok, ld, g, n_tok);
+    else
+        patchify_kernel<float><<<stream_blocks(work), 256, 0, st>>>((const float*)lat, (float*)tok, ld, g, n_tok);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpatchify(bool bf, const void* tok, int64_t ld, void* lat, const PatchGeom& g, hipStream_t st) {
+    const int64_t n_vec = (int64_t)g.T * g.H * g.W * g.C / (bf ? 8 : 4);
+    if (bf)
+        unpatchify_kernel<bf16><<<stream_blocks(n_vec), 256, 0, st>>>((const bf16*)tok, ld, (bf16*)lat, g, n_vec);
+    else
+        unpatchify_kernel<float><<<stream_blocks(n_vec), 256, 0, st>>>((const float*)tok, ld, (float*)lat, g, n_vec);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // launchers
 
 template <typename T, int VPL>

@@ -309,6 +309,63 @@ def make_inputs(cfg: BlockConfig, tensors: Sequence[str] = tuple(TENSOR_IDS)) ->
     return out
 
 
+# ---------------------------------------------------------------- adapters
+
+ADAPTER_TENSOR_IDS = {"feat": 1, "w_in": 2, "w_out": 3}
+MODALITY_IDS = {"text": 0, "video": 1, "audio": 2}
+
+
+def modality(kind: str) -> str:
+    """Interval kind -> "text", "video" (video, reference video and images)
+    or "audio" (audio and reference audio)."""
+    if kind == "text":
+        return "text"
+    if "audio" in kind:
+        return "audio"
+    if "video" in kind or "image" in kind:
+        return "video"
+    raise ValueError(f"no modality for interval kind {kind!r}")
+
+
+def adapter_shapes(cfg: BlockConfig, text_width: int, video_channels: int = 24, audio_channels: int = 32,
+                   video_patch=(1, 2, 2)) -> Dict[str, tuple]:
+    """Shapes of the adapter inputs: "feat/<kind>" -> channels-last latent
+    [T, H, W, C] of a video/audio interval ([len, text_width] for text);
+    "w_in/<modality>" -> [dim, values per token]; "w_out/<modality>" ->
+    [values per token, dim] for video and audio."""
+    pt, ph, pw = video_patch
+    width = {"text": text_width, "video": pt * ph * pw * video_channels, "audio": audio_channels}
+    out = {}
+    for s in cfg.segments:
+        m = modality(s.kind)
+        out["feat/" + s.kind] = ((s.length, text_width) if m == "text" else
+                                 (s.T * pt, s.H * ph, s.W * pw, video_channels) if m == "video" else
+                                 (s.T, s.H, s.W, audio_channels))
+        out["w_in/" + m] = (cfg.dim, width[m])
+        if m != "text":
+            out["w_out/" + m] = (width[m], cfg.dim)
+    return out
+
+
+def make_adapter_inputs(cfg: BlockConfig, text_width: int, **geom) -> Dict[str, np.ndarray]:
+    """Seeded adapter inputs: features and latents N(0,1), projections
+    N(0, w_std^2), in the stored representation of cfg.dtype.  Seed:
+    1000 * workload index + 600 + 10 * (interval or modality id) + tensor id."""
+    out = {}
+    for name, shape in adapter_shapes(cfg, text_width, **geom).items():
+        kind, key = name.split("/")
+        if kind == "feat":
+            sub = [s.kind for s in cfg.segments].index(key)
+            std = 1.0
+        else:
+            sub = MODALITY_IDS[key]
+            std = cfg.w_std
+        a = np.empty(shape, dtype=np.uint16 if cfg.dtype == "bf16" else np.float32)
+        _fill_normal(a, 1000 * cfg.index + 600 + 10 * sub + ADAPTER_TENSOR_IDS[kind], std, cfg.dtype)
+        out[name] = a
+    return out
+
+
 def draw_rows(cfg: BlockConfig, shape, seed: int, dtype: str = None) -> np.ndarray:
     """Extra seeded N(0,1) tensors (per-call parity inputs, peaked variants)."""
     out = np.empty(shape, dtype=np.uint16 if (dtype or cfg.dtype) == "bf16" else np.float32)
