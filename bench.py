@@ -31,6 +31,7 @@ METRIC = "H3 block fwd tokens/s + attention bf16 TFLOPS (% peak), 768p 15s seq"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -158,6 +159,71 @@ def device_block_weights(cfg, b):
                         rnd("mod", (inputs.N_MOD_SETS, inputs.N_MOD_CHUNKS, D), 1.0, torch.float32), gain, gain)
 
 
+def bench_fp8(args):
+    """The block's four projections as FP8 GEMMs at one workload: each step
+    quantises the activation rows (h3_quantize_fp8) and multiplies them with
+    weights quantised once per output channel (h3_gemm_fp8, bf16 out)."""
+    import torch
+
+    from video_audio_diffusion_amd import blk, inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    N, D, I, F = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn
+    shapes = {"qkv": (D, 3 * I), "o": (I, D), "gu": (D, 2 * F), "d": (F, D)}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 * cfg.index + 900)
+    bufs = {}
+    for name, (K, Nout) in shapes.items():
+        a = torch.randn(N, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        w = (torch.randn(Nout, K, generator=g, device="cuda", dtype=torch.float32) * cfg.w_std).to(torch.bfloat16)
+        qa = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+        sa = torch.empty(N, dtype=torch.float32, device="cuda")
+        qw = torch.empty(Nout, K, dtype=torch.uint8, device="cuda")
+        sw = torch.empty(Nout, dtype=torch.float32, device="cuda")
+        blk.h3_quantize_fp8(w, K, Nout, K, qw, K, sw, blk.H3_BF16)
+        c = torch.empty(N, Nout, dtype=torch.bfloat16, device="cuda")
+        bufs[name] = (a, qa, sa, qw, sw, c, K, Nout)
+        del w
+    log(f"fp8 projections of {cfg.name}: {N} tokens")
+
+    def one(ev):
+        for j, (name, (a, qa, sa, qw, sw, c, K, Nout)) in enumerate(bufs.items()):
+            if ev is not None:
+                ev[2 * j].record()
+            blk.h3_quantize_fp8(a, K, N, K, qa, K, sa, blk.H3_BF16)
+            if ev is not None:
+                ev[2 * j + 1].record()
+            blk.h3_gemm_fp8(qa, K, sa, qw, K, sw, c, Nout, N, Nout, K, blk.H3_BF16)
+        if ev is not None:
+            ev[-1].record()
+
+    for _ in range(args.warmup):
+        one(None)
+    torch.cuda.synchronize()
+    K_ = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(bufs) + 1)] for _ in range(K_)]
+    for i in range(K_):
+        one(evs[i])
+    torch.cuda.synchronize()
+    total = evs[0][0].elapsed_time(evs[-1][-1]) / K_
+    kern = {}
+    for j, (name, (a, qa, sa, qw, sw, c, K, Nout)) in enumerate(bufs.items()):
+        tq = sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in evs) / K_
+        tg = sum(e[2 * j + 1].elapsed_time(e[2 * j + 2]) for e in evs) / K_
+        fl = 2.0 * N * Nout * K
+        kern["quantize_" + name] = {"ms": round(tq, 4), "gbs": round(N * K * 3 / (tq * 1e-3) / 1e9, 1)}
+        kern["gemm_fp8_" + name] = {"ms": round(tg, 4), "tflops": round(fl / (tg * 1e-3) / 1e12, 1),
+                                    "frac_peak": round(fl / (tg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    flops = sum(2.0 * N * v[7] * v[6] for v in bufs.values())
+    result = {"metric": "H3 block projections as FP8 (e4m3) GEMMs, TFLOP/s", "value": round(flops / (total * 1e-3) / 1e12, 1),
+              "unit": "TFLOP/s", "n_gpus": 1, "steps": K_, "warmup": args.warmup, "ms_per_step": round(total, 3),
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 (bf16 out)",
+              "data": "synthetic", "config": {"workload": f"{cfg.name} projections", "tokens": N,
+                                               "shapes": {k: [N, v[1], v[0]] for k, v in shapes.items()}},
+              "kernels": kern}
+    print(json.dumps(result), flush=True)
+
+
 def bench_adapters(args):
     """The input and output adapters around the backbone at one workload:
     patchify and input projection of every interval into the packed
@@ -240,6 +306,8 @@ def main():
                     help="workload index: 1-4 one block; 5 the 50-block stack and one Euler step")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget; 0 skips it")
     ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the four projections as FP8 (e4m3) GEMMs with row-wise activation quantisation")
     ap.add_argument("--io", action="store_true",
                     help="time the input/output adapters (patchify, projections, unpatchify) of the workload")
     args = ap.parse_args()
@@ -260,6 +328,9 @@ def main():
     blk.load()
     if args.io:
         bench_adapters(args)
+        return
+    if args.fp8:
+        bench_fp8(args)
         return
     stack = None
     if args.config in inputs.STACKS:

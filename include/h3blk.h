@@ -237,6 +237,34 @@ h3_status h3_unpatchify(const void* tokens, int64_t ld, int32_t T, int32_t H, in
                         int32_t C, int32_t pt, int32_t ph, int32_t pw, void* latent,
                         h3_dtype dt, void* stream);
 
+/* FP8 variant of the projections (the pages mention only that the community
+ * runs the model in FP8 ([commentary]); gfx950 contracts OCP FP8 at twice the
+ * bf16 MFMA rate).  Format: OCP e4m3 -- sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, subnormals below 2^-6, largest finite 448, no
+ * infinities, NaN codes 0x7F / 0xFF.
+ *
+ * Row-wise quantisation: for each row i of x,
+ *   scales[i] = max_k |x[i,k]| / 448   (fp32 division; 1 for an all-zero row)
+ *   q[i,k]    = e4m3(x[i,k] / scales[i])   (fp32 division, then the nearest
+ *               e4m3 value, ties to the even code, saturating at +-448)
+ *   x      : [n_rows][K] in dt (bf16 or fp32), row stride ldx
+ *   q      : [n_rows][K] bytes, row stride ldq (a multiple of 16)
+ *   scales : fp32 [n_rows]
+ * K a multiple of 16.  Used for activations (per token) and for weights
+ * stored [out][in] (per output channel). */
+h3_status h3_quantize_fp8(const void* x, int64_t ldx, int64_t n_rows, int32_t K,
+                          void* q, int64_t ldq, float* scales, h3_dtype dt, void* stream);
+
+/* C = diag(a_scale) . (A . W^T) . diag(w_scale) with A [M][K] and W [N][K]
+ * in e4m3 (row strides lda, ldw in bytes, multiples of 16), exact products
+ * accumulated in fp32 by MFMA, scaled in fp32 and stored once in out_dt.
+ *   a_scale : fp32 [M], w_scale : fp32 [N] (as written by h3_quantize_fp8)
+ *   C       : [M][N] in out_dt, row stride ldc; must not overlap the inputs
+ * K a multiple of 128, N a multiple of 8. */
+h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const void* W,
+                      int64_t ldw, const float* w_scale, void* C, int64_t ldc, int64_t M,
+                      int32_t N, int32_t K, h3_dtype out_dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -264,3 +264,28 @@ def test_patchify_validation(lib):
         assert f(tok=lat + 64) == blk.H3_ERR_ARG              # overlaps the latent
         assert f(T=0) == blk.H3_OK                            # nothing to do
     assert pf(C=20, dt=1, ld=80) != blk.H3_ERR_SHAPE          # fp32: 4-element vectors
+
+
+def test_fp8_validation(lib):
+    L = blk.load()
+    x, q, s = P, P + (1 << 32), P + (2 << 32)
+
+    def qz(x=x, ldx=5376, n=100, K=5376, q=q, ldq=5376, s=s, dt=0):
+        return L.h3_quantize_fp8(x, ldx, n, K, q, ldq, s, dt, 0)
+    assert qz(dt=4) == blk.H3_ERR_DTYPE
+    assert qz(s=None) == blk.H3_ERR_ARG
+    assert qz(ldq=100) == blk.H3_ERR_ARG
+    assert qz(K=5370, ldx=5376) == blk.H3_ERR_SHAPE          # K a multiple of 16
+    assert qz(ldq=5380) == blk.H3_ERR_ALIGN
+    assert qz(q=x + 64) == blk.H3_ERR_ARG                    # q overlaps x
+    assert qz(n=0) == blk.H3_OK
+    A, W, C, sa, sw = P, P + (1 << 32), P + (2 << 32), P + (3 << 32), P + (4 << 32)
+
+    def g(A=A, lda=5376, sa=sa, W=W, ldw=5376, sw=sw, C=C, ldc=21504, M=100, N=21504, K=5376, dt=0):
+        return L.h3_gemm_fp8(A, lda, sa, W, ldw, sw, C, ldc, M, N, K, dt, 0)
+    assert g(dt=3) == blk.H3_ERR_DTYPE
+    assert g(sa=None) == blk.H3_ERR_ARG
+    assert g(K=5376 - 64, lda=5376, ldw=5376) == blk.H3_ERR_SHAPE   # K a multiple of 128
+    assert g(lda=5384) == blk.H3_ERR_ALIGN
+    assert g(C=A + 64) == blk.H3_ERR_ARG
+    assert g(M=0) == blk.H3_OK

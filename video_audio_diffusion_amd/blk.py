@@ -22,7 +22,8 @@ H3_MAX_SEGMENTS = 64
 
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
-           "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify")
+           "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
+           "h3_gemm_fp8")
 
 
 class H3Segment(ctypes.Structure):
@@ -52,6 +53,8 @@ _SIGS = {
     "h3_gemm_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P],
     "h3_patchify": [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P],
     "h3_unpatchify": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P],
+    "h3_quantize_fp8": [_P, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
+    "h3_gemm_fp8": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _I32, _P],
 }
 
 
@@ -144,6 +147,16 @@ def h3_patchify(latent, T, H, W, C, pt, ph, pw, tokens, ld, dt, stream=None):
 def h3_unpatchify(tokens, ld, T, H, W, C, pt, ph, pw, latent, dt, stream=None):
     _check("h3_unpatchify", load().h3_unpatchify(ptr(tokens), ld, T, H, W, C, pt, ph, pw, ptr(latent), dt,
                                                  _stream(stream)))
+
+
+def h3_quantize_fp8(x, ldx, n_rows, K, q, ldq, scales, dt, stream=None):
+    _check("h3_quantize_fp8", load().h3_quantize_fp8(ptr(x), ldx, n_rows, K, ptr(q), ldq, ptr(scales), dt,
+                                                     _stream(stream)))
+
+
+def h3_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt, stream=None):
+    _check("h3_gemm_fp8", load().h3_gemm_fp8(ptr(A), lda, ptr(a_scale), ptr(W), ldw, ptr(w_scale), ptr(C), ldc, M, N,
+                                             K, out_dt, _stream(stream)))
 
 
 def interleave_gate_up_rows(F: int):

@@ -306,4 +306,41 @@ h3_status h3_unpatchify(const void* tokens, int64_t ld, int32_t T, int32_t H, in
                                         (hipStream_t)stream));
 }
 
+h3_status h3_quantize_fp8(const void* x, int64_t ldx, int64_t n_rows, int32_t K, void* q, int64_t ldq,
+                          float* scales, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!x || !q || !scales || n_rows < 0 || K < 1 || ldx < K || ldq < K) return H3_ERR_ARG;
+    if (n_rows >= kMaxTok || K % 16) return H3_ERR_SHAPE;
+    const int es = esize(dt);
+    if (!aligned16(x) || !aligned16(q) || (ldx * es) % 16 || ldq % 16 || ((uintptr_t)scales & 3)) return H3_ERR_ALIGN;
+    const Span sq = span(q, n_rows, K, ldq, 1);
+    if (overlap(sq, span(x, n_rows, K, ldx, es)) || overlap(span(scales, 1, n_rows, 0, 4), sq) ||
+        overlap(span(scales, 1, n_rows, 0, 4), span(x, n_rows, K, ldx, es)))
+        return H3_ERR_ARG;
+    if (n_rows == 0) return H3_OK;
+    return hip_status(launch_quantize_fp8(dt == H3_BF16, x, ldx, (int32_t)n_rows, K, q, ldq, scales,
+                                          (hipStream_t)stream));
+}
+
+h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const void* W, int64_t ldw,
+                      const float* w_scale, void* C, int64_t ldc, int64_t M, int32_t N, int32_t K, h3_dtype out_dt,
+                      void* stream) {
+    if (!valid_dt(out_dt)) return H3_ERR_DTYPE;
+    if (!A || !W || !C || !a_scale || !w_scale || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
+    if (lda < K || ldw < K || ldc < N) return H3_ERR_ARG;
+    if (M >= kMaxTok || N % 8 || K % 128) return H3_ERR_SHAPE;
+    if (lda * 256 >= ((int64_t)1 << 31) || ldw * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
+    const int es = esize(out_dt);
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || lda % 16 || ldw % 16 || (ldc * es) % 16 ||
+        ((uintptr_t)a_scale & 3) || ((uintptr_t)w_scale & 3))
+        return H3_ERR_ALIGN;
+    const Span c = span(C, M, N, ldc, es);
+    if (overlap(c, span(A, M, K, lda, 1)) || overlap(c, span(W, N, K, ldw, 1)) ||
+        overlap(c, span(a_scale, 1, M, 0, 4)) || overlap(c, span(w_scale, 1, N, 0, 4)))
+        return H3_ERR_ARG;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt == H3_BF16,
+                                      (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -54,6 +54,48 @@ template <> struct GemmMfma<float> {
     __device__ __forceinline__ static float load(const float* p) { return *p; }
 };
 
+// Operand policies: bytes of K one MFMA contracts per row (one k-chunk), the
+// fragment one lane reads for it (16 bytes at offset (lane / 32) * 16 of a
+// 32-byte chunk, or 32 bytes at (lane / 32) * 32 of a 64-byte fp8 chunk --
+// the same place in A and in W, so the K order inside a chunk cancels) and
+// the MFMA.  fp8 is OCP e4m3 (v_mfma_f32_32x32x64_f8f6f4, formats 0/0,
+// unit scales).
+using fp8 = uint8_t;
+template <typename T> struct GemmOp;
+template <> struct GemmOp<bf16> {
+    static constexpr int CHUNK = 32;
+    using Frag = u32x4;
+    __device__ __forceinline__ static Frag read(const char* lo, const char* hi) {
+        (void)hi;
+        return *reinterpret_cast<const u32x4*>(lo);
+    }
+    __device__ __forceinline__ static void mma(f32x16& acc, const Frag& a, const Frag& b) { GemmMfma<bf16>::mma(acc, a, b); }
+};
+template <> struct GemmOp<float> {
+    static constexpr int CHUNK = 32;
+    using Frag = u32x4;
+    __device__ __forceinline__ static Frag read(const char* lo, const char* hi) {
+        (void)hi;
+        return *reinterpret_cast<const u32x4*>(lo);
+    }
+    __device__ __forceinline__ static void mma(f32x16& acc, const Frag& a, const Frag& b) { GemmMfma<float>::mma(acc, a, b); }
+};
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+template <> struct GemmOp<fp8> {
+    static constexpr int CHUNK = 64;
+    struct Frag { u32x4 lo, hi; };
+    __device__ __forceinline__ static Frag read(const char* lo, const char* hi) {
+        return Frag{*reinterpret_cast<const u32x4*>(lo), *reinterpret_cast<const u32x4*>(hi)};
+    }
+    __device__ __forceinline__ static void mma(f32x16& acc, const Frag& a, const Frag& b) {
+        const i32x8 av = {(int32_t)a.lo[0], (int32_t)a.lo[1], (int32_t)a.lo[2], (int32_t)a.lo[3],
+                          (int32_t)a.hi[0], (int32_t)a.hi[1], (int32_t)a.hi[2], (int32_t)a.hi[3]};
+        const i32x8 bv = {(int32_t)b.lo[0], (int32_t)b.lo[1], (int32_t)b.lo[2], (int32_t)b.lo[3],
+                          (int32_t)b.hi[0], (int32_t)b.hi[1], (int32_t)b.hi[2], (int32_t)b.hi[3]};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+    }
+};
+
 constexpr int kBM = 256, kBN = 256;
 
 // Tile geometry for ROWB bytes of K per step (64 or 128) and a STAGES-deep
@@ -61,7 +103,7 @@ constexpr int kBM = 256, kBN = 256;
 // share one 256-byte bank window, so chunk c of row r is stored at
 // c ^ ((r / (256 / ROWB)) % CPR): the 16 rows of a half-wavefront fragment
 // read then fall on 16 distinct 16-byte slots.
-template <int ROWB, int STAGES, int NWAVES>
+template <int ROWB, int STAGES, int NWAVES, int CHUNK = 32>
 struct GemmGeom {
     static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
     static constexpr int RPW = 256 / ROWB;               // rows per bank window
@@ -70,7 +112,7 @@ struct GemmGeom {
     static constexpr int NJ = NWAVES == 4 ? 4 : 2;        // 32-column W blocks per wavefront
     static constexpr int ROWS_PER_WAVE = kBM / NWAVES;   // tile rows each wavefront copies
     static constexpr int ROWS_PER_PIECE = 1024 / ROWB;
-    static constexpr int KCH = ROWB / 32;                // 32-byte MFMA k-chunks per step
+    static constexpr int KCH = ROWB / CHUNK;             // MFMA k-chunks per step
     static_assert(STAGES >= 2 && STAGES * 2 * TILE <= 160 * 1024, "LDS ring too large");
     __device__ static int slot(int row, int c) { return c ^ ((row / RPW) % CPR); }
 };
@@ -104,15 +146,20 @@ struct EpiGate {
 };
 struct EpiSwiglu {};
 
-template <typename T, int ROWB, int STAGES, int NWAVES, typename EPI>
-__global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__ A, int64_t lda,
-                                                   const T* __restrict__ W, int64_t ldw,
+// TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
+// the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
+// quantisation scales) before the epilogue.
+template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, typename EPI>
+__global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict__ A, int64_t lda,
+                                                   const TI* __restrict__ W, int64_t ldw,
                                                    T* __restrict__ C, int64_t ldc, int32_t M, int32_t N,
                                                    int32_t K, int32_t tiles_m, int32_t tiles_n, int32_t group_m,
-                                                   EPI epi) {
-    using Geo = GemmGeom<ROWB, STAGES, NWAVES>;
+                                                   EPI epi, const float* __restrict__ sa,
+                                                   const float* __restrict__ sw) {
+    using Op = GemmOp<TI>;
+    using Geo = GemmGeom<ROWB, STAGES, NWAVES, Op::CHUNK>;
     constexpr int NJ = Geo::NJ;
-    constexpr int ES = sizeof(T);
+    constexpr int ES = sizeof(TI);
     constexpr int BK = ROWB / ES;                       // elements of K per step
     constexpr int TILE = Geo::TILE, PIECES = Geo::PIECES, KCH = Geo::KCH;
     // stage s: A tile at ring + 2 s TILE, W tile right after it
@@ -153,8 +200,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
     }
     const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
     const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
-    const T* a_base = A + (int64_t)m0 * lda;
-    const T* w_base = W + (int64_t)n0 * ldw;
+    const TI* a_base = A + (int64_t)m0 * lda;
+    const TI* w_base = W + (int64_t)n0 * ldw;
     auto copy_step = [&](int ks) {
         char* st = ring + (ks % STAGES) * 2 * TILE;
         copy_operand<PIECES>(st, wave, a_base, bytes_a, va, (uint32_t)ks * ROWB);
@@ -164,9 +211,14 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
     // ---- fragment offsets: row (32 i + frow) of the wave's 128-row panel,
     //      chunk 2 kk + fhalf; the row's swizzle depends on frow only
     const int frow = lane & 31, fhalf = lane >> 5;
-    uint32_t fo[KCH];
+    constexpr int CPC = Op::CHUNK / 16;                 // 16-byte slots per k-chunk
+    uint32_t fo[KCH], fo2[KCH];
 #pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) fo[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, 2 * kk + fhalf) << 4));
+    for (int kk = 0; kk < KCH; ++kk) {
+        const int c0 = CPC * kk + fhalf * (CPC / 2);
+        fo[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0) << 4));
+        fo2[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0 + 1) << 4));
+    }
     const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
 
     f32x16 acc[4][NJ];
@@ -178,19 +230,22 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
     // Fragments are double-buffered per 32-byte k-chunk: chunk kk of a step
     // lives in register slot kk % 2 (4 A + 4 W 16-byte reads), and the next
     // chunk's reads are issued before the current chunk's 16 MFMAs.
-    u32x4 fa[2][4], fw[2][NJ];
-    auto read_chunk = [&](int ks, int kk, u32x4 (&a)[4], u32x4 (&w)[NJ]) {
+    using Frag = typename Op::Frag;
+    Frag fa[2][4], fw[2][NJ];
+    auto read_chunk = [&](int ks, int kk, Frag (&a)[4], Frag (&w)[NJ]) {
         const char* st = ring + (ks % STAGES) * 2 * TILE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(st + a_panel + i * 32 * ROWB + fo[kk]);
+        for (int i = 0; i < 4; ++i)
+            a[i] = Op::read(st + a_panel + i * 32 * ROWB + fo[kk], st + a_panel + i * 32 * ROWB + fo2[kk]);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) w[j] = *reinterpret_cast<const u32x4*>(st + w_panel + j * 32 * ROWB + fo[kk]);
+        for (int j = 0; j < NJ; ++j)
+            w[j] = Op::read(st + w_panel + j * 32 * ROWB + fo[kk], st + w_panel + j * 32 * ROWB + fo2[kk]);
     };
-    auto mfma_chunk = [&](const u32x4 (&a)[4], const u32x4 (&w)[NJ]) {
+    auto mfma_chunk = [&](const Frag (&a)[4], const Frag (&w)[NJ]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) GemmMfma<T>::mma(acc[i][j], a[i], w[j]);
+            for (int j = 0; j < NJ; ++j) Op::mma(acc[i][j], a[i], w[j]);
     };
     // Wait until step s has landed in LDS for every wavefront and this
     // wavefront's reads of the step before are done: at most the copies of
@@ -250,6 +305,25 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
 
     // ---- epilogue: accumulator (lane, r) -> row 8(r/4) + 4(lane/32) + r%4, col lane%32
     const bool full = m0 + kBM <= M && n0 + kBN <= N;
+    if constexpr (std::is_same<TI, fp8>::value) {
+        // dequantise: acc * sa[row] * sw[col] (rows and columns past M / N
+        // take scale 0 and are never stored)
+        float cs[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = n0 + wn * NJ * 32 + j * 32 + frow;
+            cs[j] = col < N ? sw[col] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                const float rs = row < M ? sa[row] : 0.f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j][r] *= rs * cs[j];
+            }
+    }
     if constexpr (std::is_same<EPI, EpiStore>::value) {
         T* cbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
         if (full) {
@@ -379,21 +453,29 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const T* __restrict__
 #define H3_GEMM_WAVES 8
 #endif
 
-template <typename EPI>
-hipError_t launch_gemm_epi(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
-                           int64_t M, int32_t N, int32_t K, const EPI& epi, hipStream_t st) {
+template <typename TI, typename TO, typename EPI>
+hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int64_t M,
+                         int32_t N, int32_t K, const EPI& epi, const float* sa, const float* sw, hipStream_t st) {
     const int tiles_m = (int)((M + kBM - 1) / kBM);
     const int tiles_n = (N + kBN - 1) / kBN;
     const int grid = tiles_m * tiles_n;
-    if (bf)
-        gemm_kernel<bf16, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
-            (const bf16*)A, lda, (const bf16*)W, ldw, (bf16*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-            H3_GEMM_GROUP_M, epi);
-    else
-        gemm_kernel<float, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
-            (const float*)A, lda, (const float*)W, ldw, (float*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-            H3_GEMM_GROUP_M, epi);
+    gemm_kernel<TI, TO, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
+        (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, H3_GEMM_GROUP_M, epi,
+        sa, sw);
     return hipGetLastError();
+}
+
+template <typename EPI>
+hipError_t launch_gemm_epi(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+                           int64_t M, int32_t N, int32_t K, const EPI& epi, hipStream_t st) {
+    return bf ? launch_gemm_t<bf16, bf16>(A, lda, W, ldw, C, ldc, M, N, K, epi, nullptr, nullptr, st)
+              : launch_gemm_t<float, float>(A, lda, W, ldw, C, ldc, M, N, K, epi, nullptr, nullptr, st);
+}
+
+hipError_t launch_gemm_fp8(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw, const float* sw,
+                           void* C, int64_t ldc, int64_t M, int32_t N, int32_t K, bool out_bf16, hipStream_t st) {
+    return out_bf16 ? launch_gemm_t<fp8, bf16>(A, lda, W, ldw, C, ldc, M, N, K, EpiStore{}, sa, sw, st)
+                    : launch_gemm_t<fp8, float>(A, lda, W, ldw, C, ldc, M, N, K, EpiStore{}, sa, sw, st);
 }
 
 hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
