@@ -67,3 +67,55 @@ def gemm_fp8(qa, sa, qw, sw):
     """C = diag(sa) (decode(qa) . decode(qw)^T) diag(sw) in fp64."""
     return linear(e4m3_decode(qa), e4m3_decode(qw)) * np.asarray(sa, np.float64)[:, None] \
         * np.asarray(sw, np.float64)[None, :]
+
+
+# ------------------------------------------------------------------ attention
+# Readings for the fp8 attention (the pages give none): q is quantised per
+# (token, head), k and v per head (their scales are constants of the head);
+# the reference is the exact softmax attention of the dequantised operands.
+# Rounding the softmax weights to e4m3 inside the kernel is an approximation
+# the tolerance covers, not part of this definition.
+
+def quantize_qkv(q, k, v, heads, head_dim):
+    """q, k, v [n, heads*head_dim] (fp32-representable) -> codes of the same
+    shape, sq [heads, n], sk [heads], sv [heads] (fp32 scales max/448)."""
+    n = np.asarray(q).shape[0]
+    q32 = np.asarray(q, np.float32).reshape(n, heads, head_dim)
+    mx = np.max(np.abs(q32), axis=2)                                     # [n, heads]
+    sq = np.where(mx > 0, mx / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q8 = e4m3_encode(q32 / sq[:, :, None]).reshape(n, heads * head_dim)
+    out = [q8, sq.T.copy()]
+    for x in (k, v):
+        x32 = np.asarray(x, np.float32).reshape(n, heads, head_dim)
+        m = np.max(np.abs(x32), axis=(0, 2))
+        s = np.where(m > 0, m / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        out += [e4m3_encode(x32 / s[None, :, None]).reshape(n, heads * head_dim), s]
+    q8, sq, k8, sk, v8, sv = out
+    return q8, sq, k8, sk, v8, sv
+
+
+def vt_key(p):
+    """Key (within its group of 64) stored at position p of the transposed
+    fp8 v: p = 32 g + b holds key 32 (b // 16) + 8 ((b % 16) // 4) + 4 g + b % 4."""
+    p = np.asarray(p)
+    g, b = p // 32, p % 32
+    return 32 * (b // 16) + 8 * ((b % 16) // 4) + 4 * g + b % 4
+
+
+def vt_layout(v8, heads, head_dim, n_pad):
+    """Codes v8 [n, heads*head_dim] -> [heads, head_dim, n_pad]: transposed,
+    each 64-key group in vt_key order, zero past n."""
+    n = v8.shape[0]
+    full = np.zeros((n_pad, heads, head_dim), np.uint8)
+    full[:n] = v8.reshape(n, heads, head_dim)
+    pos = np.arange(n_pad)
+    src = (pos // 64) * 64 + vt_key(pos % 64)
+    return full[src].transpose(1, 2, 0).copy()
+
+
+def dequantize_qkv(q8, sq, k8, sk, v8, sv, heads, head_dim):
+    n = q8.shape[0]
+    q = e4m3_decode(q8).reshape(n, heads, head_dim) * np.asarray(sq, np.float64).T[:, :, None]
+    k = e4m3_decode(k8).reshape(n, heads, head_dim) * np.asarray(sk, np.float64)[None, :, None]
+    v = e4m3_decode(v8).reshape(n, heads, head_dim) * np.asarray(sv, np.float64)[None, :, None]
+    return tuple(a.reshape(n, heads * head_dim) for a in (q, k, v))

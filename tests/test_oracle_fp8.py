@@ -101,3 +101,76 @@ def test_quantisation_error_bound():
     e_f = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert e_f <= 6e-2 and e_max <= 6e-2, (e_max, e_f)
     assert e_f >= 1e-2                                      # the operands really were quantised
+
+
+# ------------------------------------------------------------------ attention
+
+def test_qkv_quantisation_reduces_to_rows():
+    """Per (token, head) q scales are the row quantiser on each head's slice;
+    k and v take one scale per head over all tokens."""
+    g = np.random.Generator(np.random.PCG64(21))
+    n, H, d = 9, 3, 16
+    q, k, v = (g.standard_normal((n, H * d)).astype(np.float32) * (1 + i) for i in range(3))
+    q8, sq, k8, sk, v8, sv = oracle.quantize_qkv(q, k, v, H, d)
+    assert sq.shape == (H, n) and sk.shape == (H,)
+    for h in range(H):
+        qr, sr = oracle.quantize_rows(q[:, h * d:(h + 1) * d])
+        np.testing.assert_array_equal(q8[:, h * d:(h + 1) * d], qr)
+        np.testing.assert_array_equal(sq[h], sr)
+        assert sk[h] == np.float32(np.abs(k[:, h * d:(h + 1) * d]).max()) / np.float32(448)
+        assert np.max(v8[:, h * d:(h + 1) * d] & 0x7F) == 0x7E        # the head maximum lands on 448
+
+
+def test_vt_key_is_a_permutation_and_layout_inverts():
+    keys = oracle.vt_key(np.arange(64))
+    assert sorted(keys.tolist()) == list(range(64))
+    assert keys[:4].tolist() == [0, 1, 2, 3] and keys[4:8].tolist() == [8, 9, 10, 11]
+    assert keys[16:20].tolist() == [32, 33, 34, 35] and keys[32:36].tolist() == [4, 5, 6, 7]
+    g = np.random.Generator(np.random.PCG64(22))
+    n, H, d, n_pad = 100, 2, 8, 128
+    v8 = g.integers(0, 0x7F, size=(n, H * d)).astype(np.uint8)
+    vt = oracle.vt_layout(v8, H, d, n_pad)
+    assert vt.shape == (H, d, n_pad)
+    for p in (0, 5, 37, 63, 64, 99):
+        key = (p // 64) * 64 + int(oracle.vt_key(p % 64))
+        want = v8[key].reshape(H, d) if key < n else np.zeros((H, d), np.uint8)
+        np.testing.assert_array_equal(vt[:, :, p], want)
+
+
+def test_fp8_attention_reference_on_exact_codes():
+    """Operands that e4m3 holds exactly (small integers times power-of-two
+    scales) dequantise to themselves, so the reference is plain attention."""
+    g = np.random.Generator(np.random.PCG64(23))
+    n, H, d = 40, 2, 8
+    q, k, v = (g.integers(-3, 4, size=(n, H * d)).astype(np.float32) for _ in range(3))
+    q8, sq, k8, sk, v8, sv = oracle.quantize_qkv(q, k, v, H, d)
+    qd, kd, vd = oracle.dequantize_qkv(q8, sq, k8, sk, v8, sv, H, d)
+    for a, b in ((qd, q), (kd, k), (vd, v)):
+        np.testing.assert_allclose(a, b, rtol=2 ** -4, atol=1e-12)
+
+
+def test_fp8_attention_quantisation_error_bound():
+    """Quantising q, k, v moves the attention output o = sum_j p_j v_j /
+    sum_j p_j by two terms of relative size r (the RMS relative rounding of
+    one e4m3 value, about 2.5 %): sum_j p_j dv_j / sum p, and from the logit
+    error ds_j (RMS sqrt(2) r at logits of RMS 1) sum_j p_j ds_j (v_j - o) /
+    sum p.  Both scale like o itself, so |do| / |o| in the Frobenius norm is
+    about sqrt(3) r = 4.3 %, held to 6e-2.  The largest single error is
+    compared with max |v| (o averages many v and is much smaller): a
+    per-element bound of 2^-4 of the range of v."""
+    g = np.random.Generator(np.random.PCG64(24))
+    n, H, d = 300, 2, 128
+    q, k, v = (g.standard_normal((n, H * d)).astype(np.float32) for _ in range(3))
+    ref = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), H, d, d ** -0.5)
+    dq = oracle.dequantize_qkv(*oracle.quantize_qkv(q, k, v, H, d), H, d)
+    got = oracle.attention(*dq, H, d, d ** -0.5)
+    e_v = np.abs(got - ref).max() / np.abs(v).max()
+    e_f = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert e_f <= 6e-2 and e_v <= 2.0 ** -4, (e_f, e_v)
+    # a mistake of the kind the GPU layout could make (one 64-key group's
+    # values permuted) is far outside that bound
+    v_bad = np.array(v)
+    v_bad[:64] = v_bad[oracle.vt_key(np.arange(64))]
+    bad = oracle.attention(*dq[:2], oracle.dequantize_qkv(*oracle.quantize_qkv(q, k, v_bad, H, d), H, d)[2],
+                           H, d, d ** -0.5)
+    assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.15
