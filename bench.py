@@ -224,6 +224,77 @@ def bench_fp8(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_fp8_attention(args):
+    """Attention of one workload on FP8 operands: each step quantises q, k
+    and v (h3_quantize_qkv_fp8) and attends (h3_attention_fp8).  The bf16
+    kernel (h3_attention_fwd) on the same q, k, v is timed beside it."""
+    import torch
+
+    from video_audio_diffusion_amd import blk, inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    N, H, hd = cfg.n_tok, cfg.heads, cfg.head_dim
+    if cfg.dtype != "bf16" or hd != 128:
+        raise SystemExit("the fp8 attention takes bf16 q, k, v with head_dim 128")
+    I = H * hd
+    n_pad = -(-N // 64) * 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 * cfg.index + 950)
+    qkv = torch.empty(N, 3 * I, dtype=torch.bfloat16, device="cuda")
+    for c0 in range(0, N, 8192):                      # N(0, 1): q and k as after the per-head RMS norm
+        c1 = min(N, c0 + 8192)
+        qkv[c0:c1] = torch.randn(c1 - c0, 3 * I, generator=g, device="cuda", dtype=torch.float32)
+    q8 = torch.empty(N, I, dtype=torch.uint8, device="cuda")
+    k8 = torch.empty(N, I, dtype=torch.uint8, device="cuda")
+    vt = torch.empty(I, n_pad, dtype=torch.uint8, device="cuda")
+    sq = torch.empty(H, N, dtype=torch.float32, device="cuda")
+    sk = torch.empty(H, dtype=torch.float32, device="cuda")
+    sv = torch.empty(H, dtype=torch.float32, device="cuda")
+    o8 = torch.empty(N, I, dtype=torch.bfloat16, device="cuda")
+    o16 = torch.empty(N, I, dtype=torch.bfloat16, device="cuda")
+    log(f"fp8 attention of {cfg.name}: {N} tokens x {H} heads")
+
+    def one(ev):
+        if ev is not None:
+            ev[0].record()
+        blk.h3_quantize_qkv_fp8(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], 3 * I, N, H, hd, q8, k8, vt, n_pad,
+                                sq, sk, sv, blk.H3_BF16)
+        if ev is not None:
+            ev[1].record()
+        blk.h3_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o8, I, N, H, hd, cfg.scale)
+        if ev is not None:
+            ev[2].record()
+        blk.h3_attention_fwd(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], 3 * I, o16, I, N, H, hd, cfg.scale,
+                             None, blk.H3_BF16)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        one(None)
+    torch.cuda.synchronize()
+    K_ = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_)]
+    for i in range(K_):
+        one(evs[i])
+    torch.cuda.synchronize()
+    tq, ta, tb = (sum(e[j].elapsed_time(e[j + 1]) for e in evs) / K_ for j in range(3))
+    fl = 4.0 * N * N * hd * H
+    qbytes = 3 * N * I * 2 + 3 * N * I + 4 * H * N        # bf16 q, k, v read; codes and q scales written
+    kern = {"quantize_qkv_fp8": {"ms": round(tq, 4), "gbs": round(qbytes / (tq * 1e-3) / 1e9, 1)},
+            "attention_fp8": {"ms": round(ta, 4), "tflops": round(fl / (ta * 1e-3) / 1e12, 1),
+                              "frac_peak": round(fl / (ta * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)},
+            "attention_bf16": {"ms": round(tb, 4), "tflops": round(fl / (tb * 1e-3) / 1e12, 1),
+                               "frac_peak": round(fl / (tb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+    total = tq + ta
+    result = {"metric": "H3 attention on FP8 (e4m3) operands, quantisation included, TFLOP/s",
+              "value": round(fl / (total * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_,
+              "warmup": args.warmup, "ms_per_step": round(total, 3), "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "fp8-e4m3 (fp32 sums, bf16 out)", "data": "synthetic",
+              "config": {"workload": f"{cfg.name} attention", "tokens": N, "heads": H, "head_dim": hd},
+              "kernels": kern, "speedup_vs_bf16": round(tb / total, 3)}
+    print(json.dumps(result), flush=True)
+
+
 def bench_adapters(args):
     """The input and output adapters around the backbone at one workload:
     patchify and input projection of every interval into the packed
@@ -308,6 +379,8 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the four projections as FP8 (e4m3) GEMMs with row-wise activation quantisation")
+    ap.add_argument("--fp8-attn", action="store_true",
+                    help="time the attention on FP8 operands (quantise + attend) beside the bf16 kernel")
     ap.add_argument("--io", action="store_true",
                     help="time the input/output adapters (patchify, projections, unpatchify) of the workload")
     args = ap.parse_args()
@@ -328,6 +401,9 @@ def main():
     blk.load()
     if args.io:
         bench_adapters(args)
+        return
+    if args.fp8_attn:
+        bench_fp8_attention(args)
         return
     if args.fp8:
         bench_fp8(args)

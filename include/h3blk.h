@@ -265,6 +265,46 @@ h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const vo
                       int64_t ldw, const float* w_scale, void* C, int64_t ldc, int64_t M,
                       int32_t N, int32_t K, h3_dtype out_dt, void* stream);
 
+/* FP8 attention operands (same e4m3 format and rounding as h3_quantize_fp8;
+ * [notes] section 5 defines the attention, [commentary] the FP8 practice):
+ *   sq[h, i] = max_d |q[i, h, d]| / 448            (one scale per token and head)
+ *   sk[h]    = max_{i,d} |k[i, h, d]| / 448,  sv[h] likewise for v (per head)
+ *   q8[i, h*128 + d] = e4m3(q[i,h,d] / sq[h,i]),  k8 likewise with sk[h]
+ *   vt[(h*128 + d) * n_pad + 64 t + p] = e4m3(v[64 t + key(p), h, d] / sv[h])
+ *     with key(p) = 32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4 for
+ *     p = 32 g + b (v transposed, each 64-key group permuted into the order
+ *     h3_attention_fp8 packs its weights in); a position whose key is
+ *     n_tok or later holds 0.
+ * A scale is 1 where the maximum is 0.
+ *   q, k, v : bf16 [n_tok][heads*128] views with row stride ld
+ *   q8, k8  : [n_tok][heads*128] bytes;  vt : [heads][128][n_pad] bytes
+ *   sq      : fp32 [heads][n_tok];  sk, sv : fp32 [heads]
+ * head_dim 128 (else H3_ERR_SHAPE); n_pad a multiple of 64 and >= n_tok
+ * (else H3_ERR_ARG); heads <= 65535, n_tok * heads < 2^31 and
+ * n_pad * 128 < 2^32 (else H3_ERR_SHAPE); outputs must not overlap each
+ * other or the inputs (H3_ERR_ARG).  Enqueues nine kernels; sk and sv hold
+ * maxima until the last two turn them into scales. */
+h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld,
+                              int64_t n_tok, int32_t heads, int32_t head_dim, void* q8,
+                              void* k8, void* vt, int64_t n_pad, float* sq, float* sk,
+                              float* sv, h3_dtype dt, void* stream);
+
+/* Full bidirectional attention on FP8 operands (the quantised form of
+ * h3_attention_fwd, [notes] section 5): with q^, k^, v^ the dequantised
+ * values (codes times their scales),
+ *   o[i, h] = sum_j softmax_j(scale * q^[i,h] . k^[j,h]) v^[j,h],
+ * where q^.k^ and P.v^ are formed on e4m3 MFMA with fp32 sums, and the
+ * softmax weights themselves are rounded to e4m3 (scaled so that the largest
+ * is near 2^8, so weights down to about 2^-17 of it are kept); the row sums
+ * use exactly those rounded weights.  o : bf16 [n_tok][heads*128], row
+ * stride ld_o, must not overlap the operands (H3_ERR_ARG).  Operands and
+ * sizes as h3_quantize_qkv_fp8 writes them, with the same limits; scale
+ * finite and > 0 (else H3_ERR_ARG). */
+h3_status h3_attention_fp8(const void* q8, const void* k8, const void* vt, int64_t n_pad,
+                           const float* sq, const float* sk, const float* sv, void* o,
+                           int64_t ld_o, int64_t n_tok, int32_t heads, int32_t head_dim,
+                           float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

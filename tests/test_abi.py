@@ -289,3 +289,39 @@ def test_fp8_validation(lib):
     assert g(lda=5384) == blk.H3_ERR_ALIGN
     assert g(C=A + 64) == blk.H3_ERR_ARG
     assert g(M=0) == blk.H3_OK
+
+
+def test_fp8_attention_validation(lib):
+    L = blk.load()
+    q, k, v = P, P + 256, P + 512
+    q8, k8, vt, sq, sk, sv = (P + (i << 32) for i in range(1, 7))
+    o = P + (7 << 32)
+
+    def qz(q=q, k=k, v=v, ld=21504, n=1000, H=56, hd=128, q8=q8, k8=k8, vt=vt, n_pad=1024, sq=sq, sk=sk,
+           sv=sv, dt=0):
+        return L.h3_quantize_qkv_fp8(q, k, v, ld, n, H, hd, q8, k8, vt, n_pad, sq, sk, sv, dt, 0)
+    assert qz(dt=1) == blk.H3_ERR_SHAPE                        # bf16 operands only
+    assert qz(dt=4) == blk.H3_ERR_DTYPE
+    assert qz(sv=None) == blk.H3_ERR_ARG
+    assert qz(hd=64) == blk.H3_ERR_SHAPE
+    assert qz(n_pad=960) == blk.H3_ERR_ARG                     # fewer columns than tokens
+    assert qz(n_pad=1000) == blk.H3_ERR_ARG                    # not a multiple of 64
+    assert qz(ld=7000) == blk.H3_ERR_ARG                       # row narrower than the heads
+    assert qz(H=70000, ld=70000 * 128) == blk.H3_ERR_SHAPE      # grid limit on heads
+    assert qz(q=q + 2) == blk.H3_ERR_ALIGN
+    assert qz(k8=q8 + 64) == blk.H3_ERR_ARG                    # outputs overlap
+    assert qz(sq=q + 64) == blk.H3_ERR_ARG                     # output overlaps an input
+    assert qz(n=0) == blk.H3_OK
+
+    def at(q8=q8, k8=k8, vt=vt, n_pad=1024, sq=sq, sk=sk, sv=sv, o=o, ld_o=7168, n=1000, H=56, hd=128,
+           scale=128 ** -0.5):
+        return L.h3_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o, ld_o, n, H, hd, scale, 0)
+    assert at(o=None) == blk.H3_ERR_ARG
+    assert at(scale=0.0) == blk.H3_ERR_ARG
+    assert at(scale=float("inf")) == blk.H3_ERR_ARG
+    assert at(hd=64) == blk.H3_ERR_SHAPE
+    assert at(n_pad=999) == blk.H3_ERR_ARG
+    assert at(ld_o=7000) == blk.H3_ERR_ARG
+    assert at(ld_o=7172) == blk.H3_ERR_ALIGN
+    assert at(o=vt + 64) == blk.H3_ERR_ARG                     # output overlaps V^T
+    assert at(n=0) == blk.H3_OK

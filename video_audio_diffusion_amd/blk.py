@@ -23,7 +23,7 @@ H3_MAX_SEGMENTS = 64
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
            "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
-           "h3_gemm_fp8")
+           "h3_gemm_fp8", "h3_quantize_qkv_fp8", "h3_attention_fp8")
 
 
 class H3Segment(ctypes.Structure):
@@ -55,6 +55,8 @@ _SIGS = {
     "h3_unpatchify": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P],
     "h3_quantize_fp8": [_P, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
     "h3_gemm_fp8": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _I32, _P],
+    "h3_quantize_qkv_fp8": [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _I64, _P, _P, _P, _I32, _P],
+    "h3_attention_fp8": [_P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _F, _P],
 }
 
 
@@ -157,6 +159,17 @@ def h3_quantize_fp8(x, ldx, n_rows, K, q, ldq, scales, dt, stream=None):
 def h3_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt, stream=None):
     _check("h3_gemm_fp8", load().h3_gemm_fp8(ptr(A), lda, ptr(a_scale), ptr(W), ldw, ptr(w_scale), ptr(C), ldc, M, N,
                                              K, out_dt, _stream(stream)))
+
+
+def h3_quantize_qkv_fp8(q, k, v, ld, n_tok, heads, head_dim, q8, k8, vt, n_pad, sq, sk, sv, dt, stream=None):
+    _check("h3_quantize_qkv_fp8", load().h3_quantize_qkv_fp8(ptr(q), ptr(k), ptr(v), ld, n_tok, heads, head_dim,
+                                                             ptr(q8), ptr(k8), ptr(vt), n_pad, ptr(sq), ptr(sk),
+                                                             ptr(sv), dt, _stream(stream)))
+
+
+def h3_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o, ld_o, n_tok, heads, head_dim, scale, stream=None):
+    _check("h3_attention_fp8", load().h3_attention_fp8(ptr(q8), ptr(k8), ptr(vt), n_pad, ptr(sq), ptr(sk), ptr(sv),
+                                                       ptr(o), ld_o, n_tok, heads, head_dim, scale, _stream(stream)))
 
 
 def interleave_gate_up_rows(F: int):

@@ -343,4 +343,59 @@ h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const vo
                                       (hipStream_t)stream));
 }
 
+h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int64_t n_tok, int32_t heads,
+                              int32_t head_dim, void* q8, void* k8, void* vt, int64_t n_pad, float* sq, float* sk,
+                              float* sv, h3_dtype dt, void* stream) {
+    if (dt != H3_BF16) return valid_dt(dt) ? H3_ERR_SHAPE : H3_ERR_DTYPE;
+    if (!q || !k || !v || !q8 || !k8 || !vt || !sq || !sk || !sv || n_tok < 0 || heads < 1) return H3_ERR_ARG;
+    if (head_dim != 128) return H3_ERR_SHAPE;
+    const int64_t width = (int64_t)heads * 128;
+    if (ld < width || n_pad < ((n_tok + 63) / 64) * 64 || n_pad % 64) return H3_ERR_ARG;
+    if (n_tok >= kMaxTok || n_pad * 128 >= ((int64_t)1 << 32) || width * 64 >= ((int64_t)1 << 31) ||
+        heads > 65535 || n_tok * heads >= ((int64_t)1 << 31))
+        return H3_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (ld * 2) % 16 || !aligned16(q8) || !aligned16(k8) ||
+        !aligned16(vt) || ((uintptr_t)sq & 3) || ((uintptr_t)sk & 3) || ((uintptr_t)sv & 3))
+        return H3_ERR_ALIGN;
+    const Span outs[6] = {span(q8, n_tok, width, width, 1), span(k8, n_tok, width, width, 1),
+                          span(vt, (int64_t)heads * 128, n_pad, n_pad, 1), span(sq, 1, (int64_t)heads * n_tok, 0, 4),
+                          span(sk, 1, heads, 0, 4), span(sv, 1, heads, 0, 4)};
+    const Span ins[3] = {span(q, n_tok, width, ld, 2), span(k, n_tok, width, ld, 2), span(v, n_tok, width, ld, 2)};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], ins[j])) return H3_ERR_ARG;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return H3_ERR_ARG;
+    }
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_quantize_qkv_fp8(q, k, v, ld, (int32_t)n_tok, heads, q8, k8, vt, n_pad, sq, sk, sv,
+                                              (hipStream_t)stream));
+}
+
+h3_status h3_attention_fp8(const void* q8, const void* k8, const void* vt, int64_t n_pad, const float* sq,
+                           const float* sk, const float* sv, void* o, int64_t ld_o, int64_t n_tok, int32_t heads,
+                           int32_t head_dim, float scale, void* stream) {
+    if (!q8 || !k8 || !vt || !sq || !sk || !sv || !o || n_tok < 0 || heads < 1 || !isfinite(scale) ||
+        !(scale > 0.f))
+        return H3_ERR_ARG;
+    if (head_dim != 128) return H3_ERR_SHAPE;
+    const int64_t width = (int64_t)heads * 128;
+    if (ld_o < width || n_pad < ((n_tok + 63) / 64) * 64 || n_pad % 64) return H3_ERR_ARG;
+    if (n_tok >= kMaxTok || n_pad * 128 >= ((int64_t)1 << 32) || width * 64 >= ((int64_t)1 << 31) ||
+        heads > 65535 || n_tok * heads >= ((int64_t)1 << 31))
+        return H3_ERR_SHAPE;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt) || !aligned16(o) || (ld_o * 2) % 16 ||
+        ((uintptr_t)sq & 3) || ((uintptr_t)sk & 3) || ((uintptr_t)sv & 3))
+        return H3_ERR_ALIGN;
+    const Span so = span(o, n_tok, width, ld_o, 2);
+    if (overlap(so, span(q8, n_tok, width, width, 1)) || overlap(so, span(k8, n_tok, width, width, 1)) ||
+        overlap(so, span(vt, (int64_t)heads * 128, n_pad, n_pad, 1)) ||
+        overlap(so, span(sq, 1, (int64_t)heads * n_tok, 0, 4)) || overlap(so, span(sk, 1, heads, 0, 4)) ||
+        overlap(so, span(sv, 1, heads, 0, 4)))
+        return H3_ERR_ARG;
+    if (n_tok == 0) return H3_OK;
+    return hip_status(launch_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o, ld_o, (int32_t)n_tok, heads, scale,
+                                           (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -653,6 +653,257 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------- fp8 attention
+// head_dim 128, operands from the fp8 quantisation of q, k and v: Q8 and K8
+// [n][heads * 128] e4m3 codes, VT [heads][128][n_pad] (v transposed, each
+// 64-key group permuted into the byte order in which P is packed below), q
+// scales per (head, token), k and v scales per head.
+//
+// Same work split as the bf16 kernel (8 wavefronts x 32 queries) but in
+// 64-key steps on v_mfma_f32_32x32x64_f8f6f4: per step, QK of the next tile
+// (2 key halves x 2 d chunks = 4 MFMAs), the exponentials of this tile, and
+// PV (4 d blocks of 32 keys x 64 -- P^T is the B operand, 32 bytes per lane:
+// the 16 values a lane holds of each key half), plus a fifth PV MFMA whose A
+// operand is all ones, so every row of that accumulator is the row sum of
+// exactly the fp8 weights PV used.
+//
+// Softmax: x = s * sl2 * sq[query] * sk[head] - m_ref, p = 2^(x + 8): the
+// weights are kept near the top of e4m3's range (largest finite 448, smallest
+// subnormal 2^-9), so keys down to 2^-17 of the reference still count.  A
+// tile whose largest p exceeds 448 (its max moved more than 0.8 above the
+// reference) raises the reference to its max first.  The output is
+// O * sv[head] / l.
+//
+// LDS: a ring of five K tiles (64 keys x 128 bytes) and five V^T tiles (128 d
+// rows x 64 bytes), 16-byte slots XOR-swizzled by row (K: (row / 2) % 8,
+// V^T: (row / 4) % 4) so each half-wavefront fragment read hits 16 distinct
+// slots.  Tile u is read in steps u-2 (K, during PV) and u (V); its copy goes out at
+// the barrier before step u-4, into the buffer tile u-5 left (read last in
+// step u-5, so every wavefront is done with it once all have passed the
+// barrier before step u-4).
+constexpr int kF8Buf = 5;
+
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
+    const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ VT, int64_t n_pad,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    bf16* __restrict__ O, int64_t ldo, int32_t n, int32_t heads, float sl2, int32_t nqt) {
+    constexpr int KT = 64 * 128;                 // bytes of one K tile and of one V^T tile
+    typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+    __shared__ __attribute__((aligned(1024))) char kl[kF8Buf * KT];
+    __shared__ __attribute__((aligned(1024))) char vl[kF8Buf * KT];
+
+    const int G = heads * nqt;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, local = b >> 3;
+    const int base = G >> 3, extra = G & 7;
+    const int L = xcd * base + (xcd < extra ? xcd : extra) + local;
+    const int head = L / nqt;
+    const int qt = L - head * nqt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int q0 = qt * kBQ + wave * 32;
+    const int qi = q0 + col, qc = qi < n ? qi : n - 1;
+    const int64_t ldq = (int64_t)heads * 128;
+    const int NT = (n + 63) >> 6;
+
+    // Q^T fragments (B operand of QK): 32 bytes of d chunk c at g * 32
+    i32x8 qf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint8_t* src = Q8 + (int64_t)qc * ldq + head * 128 + c * 64 + g * 32;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(src), hi = *reinterpret_cast<const u32x4*>(src + 16);
+        qf[c] = (i32x8){(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+                        (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
+    }
+    const float sl2q = sl2 * sq[(int64_t)head * n + qc] * sk[head];
+
+    // fragment offsets (the swizzle depends on the lane only)
+    uint32_t ko[2][2], vo[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) ko[c][e] = (uint32_t)(col * 128 + (((4 * c + 2 * g + e) ^ ((col >> 1) & 7)) << 4));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) vo[e] = (uint32_t)(col * 64 + (((2 * g + e) ^ ((col >> 2) & 3)) << 4));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(ko[c][e]));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(vo[e]));
+
+    // copy offsets: K rows 8 wave + lane / 8 (8 slots each), V^T rows 16 wave + lane / 4 (4 slots)
+    const int krow = 8 * wave + (lane >> 3), kslot = lane & 7;
+    const uint32_t kdo = (uint32_t)(krow * ldq + head * 128 + ((kslot ^ ((krow >> 1) & 7)) << 4));
+    const int vrow = 16 * wave + (lane >> 2), vslot = lane & 3;
+    const uint32_t vdo = (uint32_t)(vrow * n_pad + ((vslot ^ ((vrow >> 2) & 3)) << 4));
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(VT + (int64_t)head * 128 * n_pad, (uint32_t)(128 * n_pad));
+    auto copy_tile = [&](int t) __attribute__((always_inline)) {
+        if (t >= NT) return;
+        const int rem = n - t * 64;
+        const int nvalid = __builtin_amdgcn_readfirstlane(rem < 64 ? rem : 64);
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(K8 + (int64_t)t * 64 * ldq, (uint32_t)(nvalid * ldq));
+        const int slot = t % kF8Buf;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, H3_LDS(kl + slot * KT + wave * 1024), 16, kdo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(vl + slot * KT + wave * 1024), 16, vdo,
+                                                 (uint32_t)(t * 64), 0, 0);
+    };
+
+    i32x8 kf[2][2];                 // K fragments of the next QK: [key half][d chunk]
+    i32x8 vf[4];                    // V^T fragments of the next PV: [d block]
+    auto rd8 = [&](const char* p0, const char* p1) __attribute__((always_inline)) -> i32x8 {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(p0), hi = *reinterpret_cast<const u32x4*>(p1);
+        return (i32x8){(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+                       (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
+    };
+    auto read_k = [&](int t, int h, int c) __attribute__((always_inline)) {
+        const char* bp = kl + (t % kF8Buf) * KT + h * 32 * 128;
+        kf[h][c] = rd8(bp + ko[c][0], bp + ko[c][1]);
+    };
+    auto read_v = [&](int t, int db) __attribute__((always_inline)) {
+        const char* bp = vl + (t % kF8Buf) * KT + db * 32 * 64;
+        vf[db] = rd8(bp + vo[0], bp + vo[1]);
+    };
+    auto mfma8 = [&](const i32x8& a, const i32x8& bb, f32x16& acc) __attribute__((always_inline)) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc, 0, 0, 0, 0, 0, 0);
+    };
+    auto mask = [&](f32x16 (&sa)[2], int kbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kbase + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3) >= n) sa[h][r] = -__builtin_inff();
+    };
+    auto tile_max = [&](const f32x16 (&sa)[2]) __attribute__((always_inline)) -> float {
+        float mx = __builtin_fmaxf(sa[0][0], sa[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sa[0][r], sa[1][r]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2q;
+    };
+
+    f32x16 oacc[5];
+#pragma unroll
+    for (int db = 0; db < 5; ++db) oacc[db] = (f32x16){};
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838};
+    float m_ref;
+    f32x16 s[2];
+
+    // weights of tile s[] as e4m3, 32 bytes per lane (key half 0 then 1);
+    // pmax = the largest weight
+    auto softmax_pack = [&](i32x8& pf, float& pmax) __attribute__((always_inline)) {
+        const float mo = m_ref - 8.0f;
+        pmax = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = fast_exp2(__builtin_fmaf(s[h][4 * w + e], sl2q, -mo));
+                    pmax = __builtin_fmaxf(pmax, p[e]);
+                }
+                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+                pf[4 * h + w] = wd;
+            }
+    };
+
+    // ---- prologue
+    zero_lds(kl, kF8Buf * KT, tid);
+    zero_lds(vl, kF8Buf * KT, tid);
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) copy_tile(t);
+    wait_vm<0, false>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) read_k(0, h, c);
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) mfma8(kf[h][c], qf[c], s[h]);
+    if (n < 64) mask(s, 0);
+    m_ref = tile_max(s);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) read_k(1, h, c);
+
+    for (int t = 0; t < NT; ++t) {
+        // tile t+2 has landed for every wavefront; tile t-1's buffer takes t+4
+        wait_vm<2, false>();
+        __builtin_amdgcn_s_barrier();
+        copy_tile(t + 4);
+        f32x16 sn[2] = {(f32x16){}, (f32x16){}};
+        i32x8 pf;
+        float pmax;
+        // QK of tile t+1; then tile t's V^T fragments, whose reads the
+        // exponentials cover
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) mfma8(kf[h][c], qf[c], sn[h]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) read_v(t, db);
+        softmax_pack(pf, pmax);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(pmax <= 448.0f)) != 0, 0)) {   // rare
+            const float m_new = __builtin_fmaxf(m_ref, tile_max(s));
+            const float alpha = fast_exp2(m_ref - m_new);
+#pragma unroll
+            for (int db = 0; db < 5; ++db) oacc[db] *= alpha;
+            m_ref = m_new;
+            softmax_pack(pf, pmax);
+        }
+        // PV of tile t, K fragments of tile t+2
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            mfma8(vf[db], pf, oacc[db]);
+            read_k(t + 2, db >> 1, db & 1);
+        }
+        mfma8(ones, pf, oacc[4]);
+        if (__builtin_expect((t + 2) * 64 > n, 0)) mask(sn, (t + 1) * 64);
+        s[0] = sn[0];
+        s[1] = sn[1];
+    }
+    wait_vm<0, true>();
+
+    if (qi < n) {
+        const float inv = sv[head] / oacc[4][0];
+        bf16* orow = O + (int64_t)qi * ldo + head * 128;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                const f32x16& a = oacc[db];
+                *reinterpret_cast<u32x2*>(orow + d) =
+                    (u32x2){pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
+                            pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
+            }
+    }
+}
+
+hipError_t launch_attention_fp8(const void* q8, const void* k8, const void* vt, int64_t n_pad, const float* sq,
+                                const float* sk, const float* sv, void* o, int64_t ldo, int32_t n, int32_t heads,
+                                float scale, hipStream_t st) {
+    const int nqt = (n + kBQ - 1) / kBQ;
+    const float sl2 = (float)((double)scale * 1.4426950408889634);
+    attn_fp8_kernel<<<nqt * heads, kAttnThreads, 0, st>>>((const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)vt,
+                                                          n_pad, sq, sk, sv, (bf16*)o, ldo, n, heads, sl2, nqt);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v, int64_t ld, void* o,
                             int64_t ldo, int32_t n, int32_t heads, int32_t hd, float scale, float* lse,
                             hipStream_t st) {

@@ -61,6 +61,153 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
     }
 }
 
+// ---------------------------------------------------------------- attention operands
+// Quantisation of q, k and v ([n][heads * 128] views, bf16) for the fp8
+// attention: q per (token, head) -- its scale folds into that query's softmax
+// multiplier -- and k and v per head, whose scales fold into constants.  v is
+// written transposed, [head][d][n_pad], with each group of 64 keys permuted
+// into the byte order in which the attention kernel packs P: position
+// p = 32 g + b of a group holds key 32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4,
+// so that every fragment of V^T is 32 contiguous bytes.  Keys past n are 0.
+
+__device__ __forceinline__ int vt_key(int p) {
+    const int g = p >> 5, b = p & 31;
+    return 32 * (b >> 4) + 8 * ((b & 15) >> 2) + 4 * g + (b & 3);
+}
+
+__global__ void zero_floats(float* a, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = 0.f;
+}
+
+// max |x| over every token of each head: one workgroup per (head, 1024-row
+// chunk); 16 lanes per row, 16 rows per pass; one atomic max per workgroup on
+// the float's bits (non-negative floats order like their bit patterns).
+__global__ __launch_bounds__(256) void absmax_heads_kernel(const bf16* __restrict__ x, int64_t ld, int32_t n,
+                                                           float* amax) {
+    const int head = blockIdx.x, r0 = blockIdx.y * 1024;
+    const int sub = threadIdx.x & 15, rr = threadIdx.x >> 4;
+    float mx = 0.f;
+    for (int r = r0 + rr; r < n && r < r0 + 1024; r += 16) {
+        float v[8];
+        Vec<bf16>::load(x + (int64_t)r * ld + head * 128 + sub * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[e]));
+    }
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, kWave));
+    __shared__ float wmax[4];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float m = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+        atomicMax(reinterpret_cast<unsigned int*>(amax + head), __float_as_uint(m));
+    }
+}
+
+__device__ __forceinline__ float scale_of(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+
+// q: 16 lanes per (token, head): the group's max, its scale, 8 codes per lane.
+__global__ __launch_bounds__(256) void quantize_q_kernel(const bf16* __restrict__ q, int64_t ld, int32_t n,
+                                                         int32_t heads, uint8_t* __restrict__ q8,
+                                                         float* __restrict__ sq) {
+    const int64_t grp = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int sub = threadIdx.x & 15;
+    if (grp >= (int64_t)n * heads) return;        // uniform across a group's 16 lanes
+    const int row = (int)(grp / heads), head = (int)(grp % heads);
+    float v[8];
+    Vec<bf16>::load(q + (int64_t)row * ld + head * 128 + sub * 8, v);
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[e]));
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, m, kWave));
+    const float sc = scale_of(mx);
+    if (sub == 0) sq[(int64_t)head * n + row] = sc;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        w0 |= e4m3_code(v[e] / sc) << (8 * e);
+        w1 |= e4m3_code(v[e + 4] / sc) << (8 * e);
+    }
+    *reinterpret_cast<u32x2*>(q8 + (int64_t)row * heads * 128 + head * 128 + sub * 8) = (u32x2){w0, w1};
+}
+
+// k: one thread per 8 values with its head's scale.
+__global__ __launch_bounds__(256) void quantize_k_kernel(const bf16* __restrict__ k, int64_t ld, int32_t n,
+                                                         int32_t heads, const float* __restrict__ amax,
+                                                         uint8_t* __restrict__ k8) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = heads * 16;
+    if (idx >= (int64_t)n * per_row) return;
+    const int row = (int)(idx / per_row), c = (int)(idx % per_row);
+    const float sc = scale_of(amax[c >> 4]);
+    float v[8];
+    Vec<bf16>::load(k + (int64_t)row * ld + c * 8, v);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        w0 |= e4m3_code(v[e] / sc) << (8 * e);
+        w1 |= e4m3_code(v[e + 4] / sc) << (8 * e);
+    }
+    *reinterpret_cast<u32x2*>(k8 + (int64_t)row * heads * 128 + c * 8) = (u32x2){w0, w1};
+}
+
+// v -> V^T: one workgroup per (64-key group, head); the group's [64][128]
+// values go through LDS, then each thread writes 16 permuted bytes of a d row.
+__global__ __launch_bounds__(256) void quantize_vt_kernel(const bf16* __restrict__ v, int64_t ld, int32_t n,
+                                                          const float* __restrict__ amax, uint8_t* __restrict__ vt,
+                                                          int64_t n_pad) {
+    const int t = blockIdx.x, head = blockIdx.y;
+    __shared__ float tile[64][129];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int item = threadIdx.x + 256 * u;        // 64 keys x 16 vectors
+        const int key = item >> 4, c = item & 15;
+        float val[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (t * 64 + key < n) Vec<bf16>::load(v + (int64_t)(t * 64 + key) * ld + head * 128 + c * 8, val);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[key][c * 8 + e] = val[e];
+    }
+    __syncthreads();
+    const float sc = scale_of(amax[head]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int item = threadIdx.x + 256 * u;        // 128 d rows x 4 slots of 16 bytes
+        const int d = item >> 2, slot = item & 3;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            w[i >> 2] |= e4m3_code(tile[vt_key(slot * 16 + i)][d] / sc) << (8 * (i & 3));
+        *reinterpret_cast<u32x4*>(vt + ((int64_t)head * 128 + d) * n_pad + t * 64 + slot * 16) =
+            (u32x4){w[0], w[1], w[2], w[3]};
+    }
+}
+
+__global__ void finalize_scales(float* a, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = scale_of(a[i]);
+}
+
+hipError_t launch_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int32_t n, int32_t heads,
+                                   void* q8, void* k8, void* vt, int64_t n_pad, float* sq, float* sk, float* sv,
+                                   hipStream_t st) {
+    const int hb = (heads + 255) / 256;
+    zero_floats<<<hb, 256, 0, st>>>(sk, heads);
+    zero_floats<<<hb, 256, 0, st>>>(sv, heads);
+    const dim3 ag(heads, (n + 1023) / 1024);
+    absmax_heads_kernel<<<ag, 256, 0, st>>>((const bf16*)k, ld, n, sk);
+    absmax_heads_kernel<<<ag, 256, 0, st>>>((const bf16*)v, ld, n, sv);
+    const int64_t groups = (int64_t)n * heads;
+    quantize_q_kernel<<<(int)((groups * 16 + 255) / 256), 256, 0, st>>>((const bf16*)q, ld, n, heads, (uint8_t*)q8, sq);
+    quantize_k_kernel<<<(int)((groups * 16 + 255) / 256), 256, 0, st>>>((const bf16*)k, ld, n, heads, sk,
+                                                                       (uint8_t*)k8);
+    quantize_vt_kernel<<<dim3((unsigned)(n_pad / 64), heads), 256, 0, st>>>((const bf16*)v, ld, n, sv, (uint8_t*)vt, n_pad);
+    finalize_scales<<<hb, 256, 0, st>>>(sk, heads);
+    finalize_scales<<<hb, 256, 0, st>>>(sv, heads);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_fp8(bool bf, const void* x, int64_t ldx, int32_t n, int32_t K, void* q, int64_t ldq,
                                float* scales, hipStream_t st) {
     const int blocks = (n + 3) / 4;

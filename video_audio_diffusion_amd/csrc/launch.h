@@ -41,6 +41,12 @@ hipError_t launch_gemm_fp8(const void* A, int64_t lda, const float* sa, const vo
                            void* C, int64_t ldc, int64_t M, int32_t N, int32_t K, bool out_bf16, hipStream_t st);
 hipError_t launch_quantize_fp8(bool bf, const void* x, int64_t ldx, int32_t n, int32_t K, void* q, int64_t ldq,
                                float* scales, hipStream_t st);
+hipError_t launch_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int32_t n, int32_t heads,
+                                   void* q8, void* k8, void* vt, int64_t n_pad, float* sq, float* sk, float* sv,
+                                   hipStream_t st);
+hipError_t launch_attention_fp8(const void* q8, const void* k8, const void* vt, int64_t n_pad, const float* sq,
+                                const float* sk, const float* sv, void* o, int64_t ldo, int32_t n, int32_t heads,
+                                float scale, hipStream_t st);
 hipError_t launch_gemm(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                        int64_t ldc, int64_t M, int32_t N, int32_t K, hipStream_t st);
 hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v, int64_t ld_qkv,
