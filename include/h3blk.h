@@ -295,7 +295,7 @@ h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64
  *   o[i, h] = sum_j softmax_j(scale * q^[i,h] . k^[j,h]) v^[j,h],
  * where q^.k^ and P.v^ are formed on e4m3 MFMA with fp32 sums, and the
  * softmax weights themselves are rounded to e4m3 (scaled so that the largest
- * is near 2^8, so weights down to about 2^-17 of it are kept); the row sums
+ * is near 16, so weights down to about 2^-13 of it are kept); the row sums
  * use exactly those rounded weights.  o : bf16 [n_tok][heads*128], row
  * stride ld_o, must not overlap the operands (H3_ERR_ARG).  Operands and
  * sizes as h3_quantize_qkv_fp8 writes them, with the same limits; scale

@@ -659,29 +659,68 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 // 64-key group permuted into the byte order in which P is packed below), q
 // scales per (head, token), k and v scales per head.
 //
-// Same work split as the bf16 kernel (8 wavefronts x 32 queries) but in
-// 64-key steps on v_mfma_f32_32x32x64_f8f6f4: per step, QK of the next tile
-// (2 key halves x 2 d chunks = 4 MFMAs), the exponentials of this tile, and
-// PV (4 d blocks of 32 keys x 64 -- P^T is the B operand, 32 bytes per lane:
-// the 16 values a lane holds of each key half), plus a fifth PV MFMA whose A
-// operand is all ones, so every row of that accumulator is the row sum of
-// exactly the fp8 weights PV used.
+// 8 wavefronts x 32 queries, 64-key tiles on v_mfma_f32_32x32x64_f8f6f4.
+// Per tile a wavefront runs two blocks:
+//   V(t): the exponentials of tile t's logits, packed to e4m3, while the K
+//         fragments of tile t+1 are read;
+//   M(t): the V^T fragments of tile t are read while QK of tile t+1 runs
+//         (2 key halves x 2 d chunks), then PV of tile t (4 d blocks of 32
+//         keys x 64 -- P^T is the B operand, 32 bytes per lane: the 16
+//         values a lane holds of each key half) and a fifth PV MFMA whose A
+//         operand is all ones, so every row of that accumulator is the row
+//         sum of exactly the fp8 weights PV used.
+// At 246+ VGPRs two wavefronts share a SIMD.  If both ran the same block at
+// the same time, one unit (matrix core or VALU) would idle, so the two
+// wavefronts of each SIMD take opposite roles: one runs half a step behind
+// the other, and a barrier ends every half step.  Each SIMD then overlaps
+// one wavefront's exponentials with the other's MFMAs.  The roles come from
+// the SIMD id the hardware reports and an LDS counter per SIMD, so they do
+// not depend on how wavefronts are placed.
 //
-// Softmax: x = s * sl2 * sq[query] * sk[head] - m_ref, p = 2^(x + 8): the
-// weights are kept near the top of e4m3's range (largest finite 448, smallest
-// subnormal 2^-9), so keys down to 2^-17 of the reference still count.  A
-// tile whose largest p exceeds 448 (its max moved more than 0.8 above the
-// reference) raises the reference to its max first.  The output is
+// Softmax: x = s * sl2 * sq[query] * sk[head] - m_ref, p = 2^(x + 4): a key
+// at the reference gets weight 16, so keys down to 2^-13 of it still count
+// (e4m3's smallest subnormal is 2^-9) and the reference may be overtaken by
+// up to 4.8 (base 2) before a weight passes 448, e4m3's largest finite
+// value; for logits of unit spread the first tile's maximum is within that
+// of the row's, so a tile rarely has to be redone.  A tile whose largest p
+// exceeds 448 raises the reference to its max first.  The output is
 // O * sv[head] / l.
 //
-// LDS: a ring of five K tiles (64 keys x 128 bytes) and five V^T tiles (128 d
+// LDS: a ring of kF8Buf K tiles (64 keys x 128 bytes) and V^T tiles (128 d
 // rows x 64 bytes), 16-byte slots XOR-swizzled by row (K: (row / 2) % 8,
 // V^T: (row / 4) % 4) so each half-wavefront fragment read hits 16 distinct
-// slots.  Tile u is read in steps u-2 (K, during PV) and u (V); its copy goes out at
-// the barrier before step u-4, into the buffer tile u-5 left (read last in
-// step u-5, so every wavefront is done with it once all have passed the
-// barrier before step u-4).
-constexpr int kF8Buf = 5;
+// slots.  Half steps are numbered h = 0, 1, ...; the leading wavefronts run
+// V(t) in half step 2t and M(t) in 2t+1, the trailing ones V(t) in 2t+1 and
+// M(t) in 2t+2.  Tile u is read in half steps 2u-2 .. 2u+2; at the start of
+// half step 2j every wavefront issues its share of tile j+kF8Buf-2 into the
+// buffer of tile j-2.  Odd half steps end with the wavefront's LDS reads
+// complete and all but its last kF8Buf-4 copies landed (tile j+2 at the end
+// of half step 2j+1), then the barrier.
+constexpr int kF8Buf = 6;
+
+// Buffer descriptor words of [base, base + bytes), stride 0, as SGPRs (the
+// layout __builtin_amdgcn_make_buffer_rsrc builds; reads past `bytes` give 0).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// LDS DMA of 16 bytes per lane: [descriptor + voff + soff] -> LDS at lds +
+// 16 * lane.  It has no register result.  Written as asm because the
+// compiler otherwise makes every later LDS read of the same array wait for
+// the copy to land, ring slot or not; the ring's own vmcnt waits and
+// barriers order it instead.  s_nop 4 covers a VALU-written descriptor
+// SGPR (readfirstlane) read by VMEM, s_nop 0 the M0 write before the DMA.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ int simd_of_wave() { return (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3); }
 
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ VT, int64_t n_pad,
@@ -691,6 +730,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
     __shared__ __attribute__((aligned(1024))) char kl[kF8Buf * KT];
     __shared__ __attribute__((aligned(1024))) char vl[kF8Buf * KT];
+    __shared__ int simd_count[4];
 
     const int G = heads * nqt;
     const int b = blockIdx.x;
@@ -740,16 +780,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     const uint32_t kdo = (uint32_t)(krow * ldq + head * 128 + ((kslot ^ ((krow >> 1) & 7)) << 4));
     const int vrow = 16 * wave + (lane >> 2), vslot = lane & 3;
     const uint32_t vdo = (uint32_t)(vrow * n_pad + ((vslot ^ ((vrow >> 2) & 3)) << 4));
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(VT + (int64_t)head * 128 * n_pad, (uint32_t)(128 * n_pad));
+    const u32x4 vr = rsrc_words(VT + (int64_t)head * 128 * n_pad, (uint32_t)(128 * n_pad));
+    const uint32_t kl0 = (uint32_t)(uintptr_t)H3_LDS(kl + wave * 1024);
+    const uint32_t vl0 = (uint32_t)(uintptr_t)H3_LDS(vl + wave * 1024);
     auto copy_tile = [&](int t) __attribute__((always_inline)) {
         if (t >= NT) return;
         const int rem = n - t * 64;
         const int nvalid = __builtin_amdgcn_readfirstlane(rem < 64 ? rem : 64);
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(K8 + (int64_t)t * 64 * ldq, (uint32_t)(nvalid * ldq));
-        const int slot = t % kF8Buf;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, H3_LDS(kl + slot * KT + wave * 1024), 16, kdo, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, H3_LDS(vl + slot * KT + wave * 1024), 16, vdo,
-                                                 (uint32_t)(t * 64), 0, 0);
+        const u32x4 kr = rsrc_words(K8 + (int64_t)t * 64 * ldq, (uint32_t)(nvalid * ldq));
+        const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(t % kF8Buf) * KT);
+        lds_dma16(kr, kl0 + slot, kdo, 0u);
+        lds_dma16(vr, vl0 + slot, vdo, (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(t * 64)));
     };
 
     i32x8 kf[2][2];                 // K fragments of the next QK: [key half][d chunk]
@@ -770,17 +811,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     auto mfma8 = [&](const i32x8& a, const i32x8& bb, f32x16& acc) __attribute__((always_inline)) {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc, 0, 0, 0, 0, 0, 0);
     };
-    auto mask = [&](f32x16 (&sa)[2], int kbase) __attribute__((always_inline)) {
+
+    f32x16 s[2];                    // logits of the tile in flight: [key half]
+    auto mask = [&](int kbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (kbase + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3) >= n) sa[h][r] = -__builtin_inff();
+                if (kbase + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s[h][r] = -__builtin_inff();
     };
-    auto tile_max = [&](const f32x16 (&sa)[2]) __attribute__((always_inline)) -> float {
-        float mx = __builtin_fmaxf(sa[0][0], sa[1][0]);
+    auto tile_max = [&]() __attribute__((always_inline)) -> float {
+        float mx = __builtin_fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sa[0][r], sa[1][r]));
+        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[0][r], s[1][r]));
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2q;
     };
@@ -791,12 +834,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838};
     float m_ref;
-    f32x16 s[2];
+    i32x8 pf;                       // the tile's weights as e4m3, 32 bytes per lane (key half 0 then 1)
 
-    // weights of tile s[] as e4m3, 32 bytes per lane (key half 0 then 1);
-    // pmax = the largest weight
-    auto softmax_pack = [&](i32x8& pf, float& pmax) __attribute__((always_inline)) {
-        const float mo = m_ref - 8.0f;
+    // pmax = the largest weight.  The first conversion of each word writes
+    // its low half only and the second its high half, so the word may start
+    // from any value.
+    auto softmax_pack = [&](float& pmax) __attribute__((always_inline)) {
+        const float mo = m_ref - 4.0f;
         pmax = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -808,19 +852,70 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
                     p[e] = fast_exp2(__builtin_fmaf(s[h][4 * w + e], sl2q, -mo));
                     pmax = __builtin_fmaxf(pmax, p[e]);
                 }
-                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_nondeterministic_value(0), false);
                 wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
                 pf[4 * h + w] = wd;
             }
     };
+    // V(t): K fragments for M(t), then tile t's weights
+    auto vblock = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) read_k(t + 1, h, c);
+        if (__builtin_expect((t + 1) * 64 > n, 0)) mask(t * 64);
+        float pmax;
+        softmax_pack(pmax);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(pmax <= 448.0f)) != 0, 0)) {   // rare
+            const float m_new = __builtin_fmaxf(m_ref, tile_max());
+            const float alpha = fast_exp2(m_ref - m_new);
+#pragma unroll
+            for (int db = 0; db < 5; ++db) oacc[db] *= alpha;
+            m_ref = m_new;
+            softmax_pack(pmax);
+        }
+    };
+    // M(t): QK of tile t+1 while tile t's V^T fragments arrive, PV of tile t
+    // (the scheduling barriers keep all four V^T reads ahead of the QK
+    // MFMAs that cover their latency, and each block inside its half step)
+    auto mblock = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) read_v(t, db);
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = (f32x16){};
+        s[1] = (f32x16){};
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) mfma8(kf[h][c], qf[c], s[h]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) mfma8(vf[db], pf, oacc[db]);
+        mfma8(ones, pf, oacc[4]);
+    };
+    auto end_even = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto end_odd = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<2 * (kF8Buf - 4), true>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // ---- prologue
+    // ---- prologue: roles, tiles 0 .. kF8Buf-3, QK of tile 0
+    if (tid < 4) simd_count[tid] = 0;
     zero_lds(kl, kF8Buf * KT, tid);
     zero_lds(vl, kF8Buf * KT, tid);
     __syncthreads();
+    int rank = 0;
+    if (lane == 0) rank = atomicAdd(&simd_count[simd_of_wave()], 1);
+    const bool trailing = (__builtin_amdgcn_readfirstlane(rank) & 1) != 0;
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) copy_tile(t);
+    for (int t = 0; t < kF8Buf - 2; ++t) copy_tile(t);
     wait_vm<0, false>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -830,51 +925,32 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) mfma8(kf[h][c], qf[c], s[h]);
-    if (n < 64) mask(s, 0);
-    m_ref = tile_max(s);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) read_k(1, h, c);
+        for (int h = 0; h < 2; ++h) mfma8(kf[h][c], qf[c], s[h]);
+    if (n < 64) mask(0);
+    m_ref = tile_max();
 
-    for (int t = 0; t < NT; ++t) {
-        // tile t+2 has landed for every wavefront; tile t-1's buffer takes t+4
-        wait_vm<2, false>();
-        __builtin_amdgcn_s_barrier();
-        copy_tile(t + 4);
-        f32x16 sn[2] = {(f32x16){}, (f32x16){}};
-        i32x8 pf;
-        float pmax;
-        // QK of tile t+1; then tile t's V^T fragments, whose reads the
-        // exponentials cover
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) mfma8(kf[h][c], qf[c], sn[h]);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) read_v(t, db);
-        softmax_pack(pf, pmax);
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(pmax <= 448.0f)) != 0, 0)) {   // rare
-            const float m_new = __builtin_fmaxf(m_ref, tile_max(s));
-            const float alpha = fast_exp2(m_ref - m_new);
-#pragma unroll
-            for (int db = 0; db < 5; ++db) oacc[db] *= alpha;
-            m_ref = m_new;
-            softmax_pack(pf, pmax);
+    // ---- 2 NT + 1 half steps, each ending in a barrier, for both roles
+    if (!trailing) {
+        for (int t = 0; t < NT; ++t) {
+            copy_tile(t + kF8Buf - 2);          // half step 2t
+            vblock(t);
+            end_even();
+            mblock(t);                          // half step 2t+1
+            end_odd();
         }
-        // PV of tile t, K fragments of tile t+2
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            mfma8(vf[db], pf, oacc[db]);
-            read_k(t + 2, db >> 1, db & 1);
+        end_even();                             // half step 2 NT
+    } else {
+        copy_tile(kF8Buf - 2);                  // half step 0
+        end_even();
+        for (int t = 0; t < NT; ++t) {
+            vblock(t);                          // half step 2t+1
+            end_odd();
+            copy_tile(t + kF8Buf - 1);          // half step 2t+2
+            mblock(t);
+            end_even();
         }
-        mfma8(ones, pf, oacc[4]);
-        if (__builtin_expect((t + 2) * 64 > n, 0)) mask(sn, (t + 1) * 64);
-        s[0] = sn[0];
-        s[1] = sn[1];
     }
     wait_vm<0, true>();
 
