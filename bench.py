@@ -295,6 +295,60 @@ def bench_fp8_attention(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_fp8_block(args):
+    """The FP8 variant of the block (H3BlockFP8: projections and attention on
+    e4m3 operands, quantisation included) at one workload; the fused bf16
+    block on the same inputs is timed beside it."""
+    import torch
+
+    from video_audio_diffusion_amd import inputs
+    from video_audio_diffusion_amd.block import BlockWeights, H3Block, H3BlockFP8, device_inputs, interleave_gate_up
+
+    cfg = inputs.CONFIGS[args.config]
+    log(f"fp8 block of {cfg.name}: {cfg.n_tok} tokens; drawing inputs")
+    dev = device_inputs(cfg, inputs.make_inputs(cfg))
+    w = interleave_gate_up(BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
+                                        dev["gamma_q"], dev["gamma_k"]))
+    blocks = {"fp8": H3BlockFP8(cfg, w), "bf16": H3Block(cfg, w, fused=True)}
+    x = dev["x"]
+    K_ = args.steps
+    times, per = {}, {}
+    for name, block in blocks.items():
+        for _ in range(args.warmup):
+            block.forward(x)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(block.steps) + 1)] for _ in range(K_)]
+        for i in range(K_):
+            block.forward(x, events=ev[i])
+        torch.cuda.synchronize()
+        times[name] = ev[0][0].elapsed_time(ev[-1][-1]) / K_
+        per[name] = {st: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K_ for j, st in enumerate(block.steps)}
+        log(f"{name}: {times[name]:.2f} ms per block")
+    fl = step_flops(cfg)
+    N, D, I, F = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn
+    qbytes = {"quant_a": N * D * 3, "quant_a2": N * D * 3, "quant_o": N * I * 3, "quant_h": N * F * 3,
+              "quant_qkv": 3 * N * I * 3}
+    sbytes = step_bytes(cfg)
+    kern = {}
+    for st, ms in per["fp8"].items():
+        k = {"ms": round(ms, 4)}
+        if st in fl:
+            tf = fl[st] / (ms * 1e-3) / 1e12
+            k.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        elif st in qbytes or st in sbytes:
+            gbs = qbytes.get(st, sbytes.get(st, 0)) / (ms * 1e-3) / 1e9
+            k.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kern[st] = k
+    result = {"metric": "H3 block fwd tokens/s, FP8 (e4m3) projections and attention", "unit": "tokens/s",
+              "value": round(cfg.n_tok / (times["fp8"] * 1e-3), 1), "n_gpus": 1, "steps": K_, "warmup": args.warmup,
+              "ms_per_step": round(times["fp8"], 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "fp8-e4m3 (fp32 sums, bf16 activations)", "data": "synthetic",
+              "config": {"workload": f"{cfg.name} block forward", "tokens": cfg.n_tok},
+              "kernels": kern, "bf16_fused_block_ms": round(times["bf16"], 3),
+              "speedup_vs_bf16": round(times["bf16"] / times["fp8"], 3)}
+    print(json.dumps(result), flush=True)
+
+
 def bench_adapters(args):
     """The input and output adapters around the backbone at one workload:
     patchify and input projection of every interval into the packed
@@ -379,6 +433,8 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the four projections as FP8 (e4m3) GEMMs with row-wise activation quantisation")
+    ap.add_argument("--fp8-block", action="store_true",
+                    help="time the FP8 block (projections and attention on e4m3) beside the fused bf16 block")
     ap.add_argument("--fp8-attn", action="store_true",
                     help="time the attention on FP8 operands (quantise + attend) beside the bf16 kernel")
     ap.add_argument("--io", action="store_true",
@@ -401,6 +457,9 @@ def main():
     blk.load()
     if args.io:
         bench_adapters(args)
+        return
+    if args.fp8_block:
+        bench_fp8_block(args)
         return
     if args.fp8_attn:
         bench_fp8_attention(args)

@@ -265,6 +265,25 @@ h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const vo
                       int64_t ldw, const float* w_scale, void* C, int64_t ldc, int64_t M,
                       int32_t N, int32_t K, h3_dtype out_dt, void* stream);
 
+/* The fp8 forms of the fused projections (h3_gemm_gate_residual and
+ * h3_gemm_swiglu, [notes] section 3 and 3.2) for the FP8 variant of the
+ * block ([commentary]): the product of h3_gemm_fp8 (e4m3 codes with their
+ * row scales, fp32 sums, scaled in fp32) enters the same epilogue,
+ *   out[i,:] = x[i,:] + gate[s(i)] * (diag(a_scale) A W^T diag(w_scale))[i,:]
+ *   H[i,f]   = SiLU(g_if) * u_if with g, u the scaled gate and up products,
+ * bf16 x, out and H.  Wgu and w_scale of the SwiGLU form are the gate/up
+ * codes and their scales with rows in h3_gemm_swiglu's 32-row interleave.
+ * Argument rules of h3_gemm_fp8 (K a multiple of 128), h3_gemm_gate_residual
+ * and h3_gemm_swiglu apply; x must not overlap A. */
+h3_status h3_gemm_fp8_gate_residual(const void* A, int64_t lda, const float* a_scale, const void* W,
+                                    int64_t ldw, const float* w_scale, const void* x, void* out,
+                                    int64_t ldo, int64_t M, int32_t N, int32_t K, const float* mod,
+                                    int32_t n_sets, h3_branch br, const h3_segment* segs,
+                                    int32_t n_segs, void* stream);
+h3_status h3_gemm_fp8_swiglu(const void* A, int64_t lda, const float* a_scale, const void* Wgu,
+                             int64_t ldw, const float* w_scale, void* H, int64_t ldh, int64_t M,
+                             int32_t F, int32_t K, void* stream);
+
 /* FP8 attention operands (same e4m3 format and rounding as h3_quantize_fp8;
  * [notes] section 5 defines the attention, [commentary] the FP8 practice):
  *   sq[h, i] = max_d |q[i, h, d]| / 448            (one scale per token and head)

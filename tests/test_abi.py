@@ -325,3 +325,28 @@ def test_fp8_attention_validation(lib):
     assert at(ld_o=7172) == blk.H3_ERR_ALIGN
     assert at(o=vt + 64) == blk.H3_ERR_ARG                     # output overlaps V^T
     assert at(n=0) == blk.H3_OK
+
+
+def test_fp8_fused_projection_validation(lib):
+    L = blk.load()
+    A, W, x, out, sa, sw, mod = (P + (i << 32) for i in range(7))
+    seg = blk.segments([inputs.Segment(start=0, length=100, mod_set=0, T=100, kind="audio")])
+
+    def g(A=A, lda=7168, sa=sa, W=W, ldw=7168, sw=sw, x=x, out=out, ldo=5376, M=100, N=5376, K=7168, mod=mod,
+          n_sets=1, br=0, segs=seg, n_segs=1):
+        return L.h3_gemm_fp8_gate_residual(A, lda, sa, W, ldw, sw, x, out, ldo, M, N, K, mod, n_sets, br, segs, n_segs, 0)
+    assert g(sa=None) == blk.H3_ERR_ARG
+    assert g(K=7168 - 64) == blk.H3_ERR_SHAPE                  # K a multiple of 128
+    assert g(br=5) == blk.H3_ERR_ARG
+    assert g(x=A + 64) == blk.H3_ERR_ARG                       # x overlaps A
+    assert g(out=x + 64) == blk.H3_ERR_ARG                     # out partially overlaps x
+    assert g(x=out) != blk.H3_ERR_ARG                          # in place is allowed
+    assert g(n_segs=0) == blk.H3_ERR_SEGMENTS                  # intervals must cover the rows
+
+    def s(A=A, lda=5376, sa=sa, W=W, ldw=5376, sw=sw, H=out, ldh=14336, M=100, F=14336, K=5376):
+        return L.h3_gemm_fp8_swiglu(A, lda, sa, W, ldw, sw, H, ldh, M, F, K, 0)
+    assert s(sw=None) == blk.H3_ERR_ARG
+    assert s(F=14336 + 16) == blk.H3_ERR_SHAPE                 # F a multiple of 32
+    assert s(ldh=100) == blk.H3_ERR_ARG
+    assert s(H=A + 64) == blk.H3_ERR_ARG                       # H overlaps A
+    assert s(M=0) == blk.H3_OK

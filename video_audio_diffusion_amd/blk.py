@@ -23,7 +23,8 @@ H3_MAX_SEGMENTS = 64
 EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope3d",
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
            "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
-           "h3_gemm_fp8", "h3_quantize_qkv_fp8", "h3_attention_fp8")
+           "h3_gemm_fp8", "h3_gemm_fp8_gate_residual", "h3_gemm_fp8_swiglu", "h3_quantize_qkv_fp8",
+           "h3_attention_fp8")
 
 
 class H3Segment(ctypes.Structure):
@@ -55,6 +56,9 @@ _SIGS = {
     "h3_unpatchify": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P],
     "h3_quantize_fp8": [_P, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
     "h3_gemm_fp8": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _I32, _P],
+    "h3_gemm_fp8_gate_residual": [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P,
+                                  _I32, _P],
+    "h3_gemm_fp8_swiglu": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P],
     "h3_quantize_qkv_fp8": [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _I64, _P, _P, _P, _I32, _P],
     "h3_attention_fp8": [_P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _F, _P],
 }
@@ -159,6 +163,18 @@ def h3_quantize_fp8(x, ldx, n_rows, K, q, ldq, scales, dt, stream=None):
 def h3_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt, stream=None):
     _check("h3_gemm_fp8", load().h3_gemm_fp8(ptr(A), lda, ptr(a_scale), ptr(W), ldw, ptr(w_scale), ptr(C), ldc, M, N,
                                              K, out_dt, _stream(stream)))
+
+
+def h3_gemm_fp8_gate_residual(A, lda, a_scale, W, ldw, w_scale, x, out, ldo, M, N, K, mod, n_sets, br, segs, n_segs,
+                              stream=None):
+    _check("h3_gemm_fp8_gate_residual",
+           load().h3_gemm_fp8_gate_residual(ptr(A), lda, ptr(a_scale), ptr(W), ldw, ptr(w_scale), ptr(x), ptr(out), ldo,
+                                            M, N, K, ptr(mod), n_sets, br, segs, n_segs, _stream(stream)))
+
+
+def h3_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K, stream=None):
+    _check("h3_gemm_fp8_swiglu", load().h3_gemm_fp8_swiglu(ptr(A), lda, ptr(a_scale), ptr(Wgu), ldw, ptr(w_scale),
+                                                           ptr(H), ldh, M, F, K, _stream(stream)))
 
 
 def h3_quantize_qkv_fp8(q, k, v, ld, n_tok, heads, head_dim, q8, k8, vt, n_pad, sq, sk, sv, dt, stream=None):

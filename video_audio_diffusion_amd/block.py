@@ -1,5 +1,6 @@
-"""One H3-Omni-Transformer block forward as eleven libh3blk calls, or as
-eight with the fused projection epilogues.
+"""One H3-Omni-Transformer block forward as eleven libh3blk calls, as
+eight with the fused projection epilogues, or (H3BlockFP8) as thirteen with
+FP8 projections and attention.
 
 This driver only allocates device buffers (torch) and issues the calls in
 the block order of the "MiniMax-H3: native audio-video joint generation"
@@ -150,6 +151,103 @@ class H3Block:
         blk.h3_gemm_gate_residual(b["h"], F, w.w_d, F, b["x1"], b["out"], D, N, D, F, w.mod, nset,
                                   blk.H3_BRANCH_FFN, segs, ns, dt, st)
         rec(8)
+        return b["out"]
+
+
+def quantize_rows_fp8(w, stream: Optional[int] = None):
+    """A bf16 [rows, K] device tensor -> (e4m3 codes [rows, K] uint8, fp32
+    scale per row) by h3_quantize_fp8 (weights: one scale per output
+    channel)."""
+    import torch
+    rows, K = w.shape
+    q = torch.empty(rows, K, dtype=torch.uint8, device=w.device)
+    sc = torch.empty(rows, dtype=torch.float32, device=w.device)
+    blk.h3_quantize_fp8(w, w.stride(0), rows, K, q, K, sc, blk.H3_BF16, stream)
+    return q, sc
+
+
+class H3BlockFP8:
+    """The block with its four projections and its attention on FP8 (OCP
+    e4m3) operands -- the quantised variant of the fused block: every GEMM
+    input is quantised per row just before its GEMM (weights once, per
+    output channel, at construction), q/k/v per token-head and per head; the
+    norms, RoPE, the softmax's sums and every epilogue stay in fp32/bf16.
+
+    Buffers beyond the fused block's: a8/sa (quantised a and a2), q8, k8,
+    vt, sq, sk, sv (attention operands), o8/so, h8/sh.  bf16, head_dim 128,
+    D, I and F multiples of 128."""
+
+    STEPS = ("adaln_attn", "quant_a", "gemm_qkv", "qknorm_rope", "quant_qkv", "attention", "quant_o",
+             "gemm_o_gate", "adaln_ffn", "quant_a2", "gemm_gu_swiglu", "quant_h", "gemm_d_gate")
+
+    def __init__(self, cfg, weights: BlockWeights, device="cuda"):
+        import torch
+        if cfg.dtype != "bf16" or cfg.head_dim != 128 or any(v % 128 for v in (cfg.dim, cfg.inner, cfg.ffn)):
+            raise ValueError("the FP8 block takes bf16, head_dim 128 and widths that are multiples of 128")
+        if weights.w_gu_il is None:
+            raise ValueError("the FP8 block needs interleaved gate/up weights (interleave_gate_up)")
+        self.cfg, self.w = cfg, weights
+        self.steps = self.STEPS
+        N, D, I, F, H = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn, cfg.heads
+        self.n_pad = -(-N // 64) * 64
+        self.wq = {"qkv": quantize_rows_fp8(weights.w_qkv), "o": quantize_rows_fp8(weights.w_o),
+                   "gu": quantize_rows_fp8(weights.w_gu_il), "d": quantize_rows_fp8(weights.w_d)}
+        b16 = lambda *sh: torch.empty(*sh, dtype=torch.bfloat16, device=device)
+        u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device=device)
+        f32 = lambda *sh: torch.empty(*sh, dtype=torch.float32, device=device)
+        self.buf: Dict[str, object] = {
+            "a": b16(N, D), "qkv": b16(N, 3 * I), "o": b16(N, I), "x1": b16(N, D), "h": b16(N, F), "out": b16(N, D),
+            "a8": u8(N, D), "sa": f32(N), "q8": u8(N, I), "k8": u8(N, I), "vt": u8(I, self.n_pad),
+            "sq": f32(H, N), "sk": f32(H), "sv": f32(H), "o8": u8(N, I), "so": f32(N), "h8": u8(N, F), "sh": f32(N)}
+        self.segs = blk.segments(cfg.segments)
+        self.n_segs = len(cfg.segments)
+        self.n_sets = int(weights.mod.shape[0])
+
+    def forward(self, x, stream: Optional[int] = None, events=None):
+        """Run the block on x [N, D]; returns the `out` buffer (x may be it).
+        With `events` (len(STEPS) + 1 torch.cuda.Event), event i is recorded
+        before step i and the last after the final step."""
+        c, b, w, wq = self.cfg, self.buf, self.w, self.wq
+        N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
+        segs, ns, nset = self.segs, self.n_segs, self.n_sets
+        BF = blk.H3_BF16
+        st = blk.current_stream() if stream is None else stream
+        qkv = b["qkv"]
+        q, k, v = qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:]
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+
+        rec(0)
+        blk.h3_adaln_modulate(x, b["a"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, c.eps, BF, st)
+        rec(1)
+        blk.h3_quantize_fp8(b["a"], D, N, D, b["a8"], D, b["sa"], BF, st)
+        rec(2)
+        blk.h3_gemm_fp8(b["a8"], D, b["sa"], wq["qkv"][0], D, wq["qkv"][1], qkv, 3 * I, N, 3 * I, D, BF, st)
+        rec(3)
+        blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base,
+                             segs, ns, BF, st)
+        rec(4)
+        blk.h3_quantize_qkv_fp8(q, k, v, 3 * I, N, H, d, b["q8"], b["k8"], b["vt"], self.n_pad, b["sq"], b["sk"],
+                                b["sv"], BF, st)
+        rec(5)
+        blk.h3_attention_fp8(b["q8"], b["k8"], b["vt"], self.n_pad, b["sq"], b["sk"], b["sv"], b["o"], I, N, H, d,
+                             c.scale, st)
+        rec(6)
+        blk.h3_quantize_fp8(b["o"], I, N, I, b["o8"], I, b["so"], BF, st)
+        rec(7)
+        blk.h3_gemm_fp8_gate_residual(b["o8"], I, b["so"], wq["o"][0], I, wq["o"][1], x, b["x1"], D, N, D, I, w.mod,
+                                      nset, blk.H3_BRANCH_ATTN, segs, ns, st)
+        rec(8)
+        blk.h3_adaln_modulate(b["x1"], b["a"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, c.eps, BF, st)
+        rec(9)
+        blk.h3_quantize_fp8(b["a"], D, N, D, b["a8"], D, b["sa"], BF, st)
+        rec(10)
+        blk.h3_gemm_fp8_swiglu(b["a8"], D, b["sa"], wq["gu"][0], D, wq["gu"][1], b["h"], F, N, F, D, st)
+        rec(11)
+        blk.h3_quantize_fp8(b["h"], F, N, F, b["h8"], F, b["sh"], BF, st)
+        rec(12)
+        blk.h3_gemm_fp8_gate_residual(b["h8"], F, b["sh"], wq["d"][0], F, wq["d"][1], b["x1"], b["out"], D, N, D, F,
+                                      w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, st)
+        rec(13)
         return b["out"]
 
 

@@ -322,25 +322,72 @@ h3_status h3_quantize_fp8(const void* x, int64_t ldx, int64_t n_rows, int32_t K,
                                           (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the fp8 GEMMs: A [M][K] and W [N][K] e4m3 codes with
+// their scales, C [M][Ncols] of element size es.
+h3_status check_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const void* W, int64_t ldw,
+                         const float* w_scale, const void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                         int32_t Ncols, int es) {
+    if (!A || !W || !C || !a_scale || !w_scale || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
+    if (lda < K || ldw < K || ldc < Ncols) return H3_ERR_ARG;
+    if (M >= kMaxTok || N % 8 || K % 128) return H3_ERR_SHAPE;
+    if (lda * 256 >= ((int64_t)1 << 31) || ldw * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || lda % 16 || ldw % 16 || (ldc * es) % 16 ||
+        ((uintptr_t)a_scale & 3) || ((uintptr_t)w_scale & 3))
+        return H3_ERR_ALIGN;
+    const Span c = span(C, M, Ncols, ldc, es);
+    if (overlap(c, span(A, M, K, lda, 1)) || overlap(c, span(W, N, K, ldw, 1)) ||
+        overlap(c, span(a_scale, 1, M, 0, 4)) || overlap(c, span(w_scale, 1, N, 0, 4)))
+        return H3_ERR_ARG;
+    return H3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const void* W, int64_t ldw,
                       const float* w_scale, void* C, int64_t ldc, int64_t M, int32_t N, int32_t K, h3_dtype out_dt,
                       void* stream) {
     if (!valid_dt(out_dt)) return H3_ERR_DTYPE;
-    if (!A || !W || !C || !a_scale || !w_scale || M < 0 || N < 1 || K < 1) return H3_ERR_ARG;
-    if (lda < K || ldw < K || ldc < N) return H3_ERR_ARG;
-    if (M >= kMaxTok || N % 8 || K % 128) return H3_ERR_SHAPE;
-    if (lda * 256 >= ((int64_t)1 << 31) || ldw * 256 >= ((int64_t)1 << 31)) return H3_ERR_SHAPE;
-    const int es = esize(out_dt);
-    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || lda % 16 || ldw % 16 || (ldc * es) % 16 ||
-        ((uintptr_t)a_scale & 3) || ((uintptr_t)w_scale & 3))
-        return H3_ERR_ALIGN;
-    const Span c = span(C, M, N, ldc, es);
-    if (overlap(c, span(A, M, K, lda, 1)) || overlap(c, span(W, N, K, ldw, 1)) ||
-        overlap(c, span(a_scale, 1, M, 0, 4)) || overlap(c, span(w_scale, 1, N, 0, 4)))
-        return H3_ERR_ARG;
+    const h3_status st = check_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, N, esize(out_dt));
+    if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
     return hip_status(launch_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt == H3_BF16,
                                       (hipStream_t)stream));
+}
+
+h3_status h3_gemm_fp8_gate_residual(const void* A, int64_t lda, const float* a_scale, const void* W, int64_t ldw,
+                                    const float* w_scale, const void* x, void* out, int64_t ldo, int64_t M, int32_t N,
+                                    int32_t K, const float* mod, int32_t n_sets, h3_branch br, const h3_segment* segs,
+                                    int32_t n_segs, void* stream) {
+    h3_status st = check_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, out, ldo, M, N, K, N, 2);
+    if (st != H3_OK) return st;
+    if (!x || !mod || n_sets < 1 || !valid_branch(br)) return H3_ERR_ARG;
+    if (!aligned16(x) || !aligned16(mod)) return H3_ERR_ALIGN;
+    const Span so = span(out, M, N, ldo, 2);
+    if (out != x && overlap(so, span(x, M, N, ldo, 2))) return H3_ERR_ARG;
+    if (overlap(span(x, M, N, ldo, 2), span(A, M, K, lda, 1))) return H3_ERR_ARG;
+    SegTable tab;
+    st = build_segs(segs, n_segs, M, n_sets, &tab);
+    if (st != H3_OK) return st;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm_fp8_gate(A, lda, a_scale, W, ldw, w_scale, x, out, ldo, M, N, K, mod, n_sets,
+                                           (int32_t)br, tab, (hipStream_t)stream));
+}
+
+h3_status h3_gemm_fp8_swiglu(const void* A, int64_t lda, const float* a_scale, const void* Wgu, int64_t ldw,
+                             const float* w_scale, void* H, int64_t ldh, int64_t M, int32_t F, int32_t K, void* stream) {
+    if (F < 1 || F > (1 << 29)) return H3_ERR_ARG;
+    if (F % 32) return H3_ERR_SHAPE;
+    const h3_status st = check_gemm_fp8(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, 2 * F, K, F, 2);
+    if (st != H3_OK) return st;
+    if (M == 0) return H3_OK;
+    return hip_status(launch_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K,
+                                             (hipStream_t)stream));
 }
 
 h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int64_t n_tok, int32_t heads,

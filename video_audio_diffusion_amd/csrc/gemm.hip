@@ -499,4 +499,22 @@ hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* W
     return launch_gemm_epi(bf, A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, EpiSwiglu{}, st);
 }
 
+hipError_t launch_gemm_fp8_gate(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,
+                                const float* sw, const void* x, void* out, int64_t ldo, int64_t M, int32_t N,
+                                int32_t K, const float* mod, int32_t n_sets, int32_t br, const SegTable& tab,
+                                hipStream_t st) {
+    EpiGate e;
+    e.x = x;
+    e.mod = mod;
+    e.chunk = 3 * br + 2;
+    e.tab = tab;
+    return launch_gemm_t<fp8, bf16>(A, lda, W, ldw, out, ldo, M, N, K, e, sa, sw, st);
+}
+
+hipError_t launch_gemm_fp8_swiglu(const void* A, int64_t lda, const float* sa, const void* Wgu, int64_t ldw,
+                                  const float* sw, void* H, int64_t ldh, int64_t M, int32_t F, int32_t K,
+                                  hipStream_t st) {
+    return launch_gemm_t<fp8, bf16>(A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, EpiSwiglu{}, sa, sw, st);
+}
+
 }  // namespace h3

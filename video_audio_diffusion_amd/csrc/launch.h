@@ -39,6 +39,13 @@ hipError_t launch_patchify(bool bf, const void* lat, void* tok, int64_t ld, cons
 hipError_t launch_unpatchify(bool bf, const void* tok, int64_t ld, void* lat, const PatchGeom& g, hipStream_t st);
 hipError_t launch_gemm_fp8(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw, const float* sw,
                            void* C, int64_t ldc, int64_t M, int32_t N, int32_t K, bool out_bf16, hipStream_t st);
+hipError_t launch_gemm_fp8_gate(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,
+                                const float* sw, const void* x, void* out, int64_t ldo, int64_t M, int32_t N,
+                                int32_t K, const float* mod, int32_t n_sets, int32_t br, const SegTable& tab,
+                                hipStream_t st);
+hipError_t launch_gemm_fp8_swiglu(const void* A, int64_t lda, const float* sa, const void* Wgu, int64_t ldw,
+                                  const float* sw, void* H, int64_t ldh, int64_t M, int32_t F, int32_t K,
+                                  hipStream_t st);
 hipError_t launch_quantize_fp8(bool bf, const void* x, int64_t ldx, int32_t n, int32_t K, void* q, int64_t ldq,
                                float* scales, hipStream_t st);
 hipError_t launch_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int32_t n, int32_t heads,
