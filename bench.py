@@ -349,6 +349,88 @@ def bench_fp8_block(args):
     print(json.dumps(result), flush=True)
 
 
+def shard_config(cfg, P):
+    """One GPU's token shard of `cfg` at P GPUs: ceil(N/P) rows at full width,
+    laid out as the sequence's first rows (text, audio, whole video frames,
+    the rest as a second audio interval)."""
+    import dataclasses
+
+    from video_audio_diffusion_amd import inputs
+
+    n = -(-cfg.n_tok // P)
+    text, audio = cfg.segments[0], cfg.segments[1]
+    video = cfg.segments[-1]
+    left = n - text.length - audio.length
+    frames = max(0, left // (video.H * video.W))
+    rest = left - frames * video.H * video.W
+    parts = [("text", text.mod_set, text.length, 1, 1), ("audio", audio.mod_set, audio.length, 1, 1)]
+    if frames:
+        parts.append(("video", video.mod_set, frames, video.H, video.W))
+    if rest:
+        parts.append(("audio", audio.mod_set, rest, 1, 1))
+    return dataclasses.replace(cfg, name=f"{cfg.name} shard 1/{P}", segments=inputs.pack(parts))
+
+
+def bench_shard(args):
+    """One GPU's share of the block at P GPUs (sequence parallel, one
+    all-to-all each way around attention): the row-wise steps of the fused
+    block on ceil(N/P) tokens at full width, and attention with 56/P heads
+    over all N keys.  The exchange itself is not run (one GPU)."""
+    import torch
+
+    from video_audio_diffusion_amd import blk, inputs
+    from video_audio_diffusion_amd.block import BlockWeights, H3Block, device_inputs, interleave_gate_up
+
+    cfg = inputs.CONFIGS[args.config]
+    P = args.shard
+    if cfg.heads % P:
+        raise SystemExit(f"{cfg.heads} heads do not split over {P} GPUs")
+    scfg = shard_config(cfg, P)
+    log(f"one GPU's share at P = {P}: {scfg.n_tok} tokens row-wise, {cfg.heads // P} heads over {cfg.n_tok} keys")
+    dev = device_inputs(scfg, inputs.make_inputs(scfg))
+    w = interleave_gate_up(BlockWeights(dev["w_qkv"], dev["w_o"], dev["w_gu"], dev["w_d"], dev["mod"],
+                                        dev["gamma_q"], dev["gamma_k"]), keep_plain=False)
+    block = H3Block(scfg, w, fused=True)
+    Hs, d, N = cfg.heads // P, cfg.head_dim, cfg.n_tok
+    Is = Hs * d
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 * cfg.index + 960)
+    qkv = torch.randn(N, 3 * Is, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o = torch.empty(N, Is, dtype=torch.bfloat16, device="cuda")
+
+    def attend():
+        blk.h3_attention_fwd(qkv[:, :Is], qkv[:, Is:2 * Is], qkv[:, 2 * Is:], 3 * Is, o, Is, N, Hs, d, cfg.scale,
+                             None, blk.H3_BF16)
+
+    for _ in range(args.warmup):
+        block.forward(dev["x"])
+        attend()
+    torch.cuda.synchronize()
+    K_ = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(block.steps) + 2)] for _ in range(K_)]
+    for i in range(K_):
+        block.forward(dev["x"], events=ev[i][:-1])
+        attend()
+        ev[i][-1].record()
+    torch.cuda.synchronize()
+    steps = {st: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K_ for j, st in enumerate(block.steps)}
+    attn_ms = sum(e[-2].elapsed_time(e[-1]) for e in ev) / K_
+    row_ms = sum(ms for st, ms in steps.items() if st != "attention")
+    share_ms = row_ms + attn_ms
+    fl = 4.0 * N * N * Hs * d
+    result = {"metric": f"one GPU's compute share of the block at P = {P} (sequence parallel)", "unit": "ms",
+              "value": round(share_ms, 3), "n_gpus": 1, "steps": K_, "warmup": args.warmup,
+              "higher_is_better": False, "scaling": "strong", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic",
+              "config": {"workload": f"{cfg.name}, 1/{P} share", "rowwise_tokens": scfg.n_tok,
+                         "attention_heads": Hs, "keys": N},
+              "rowwise_ms": round(row_ms, 3), "attention_ms": round(attn_ms, 3),
+              "attention_tflops": round(fl / (attn_ms * 1e-3) / 1e12, 1),
+              "rowwise_steps_ms": {st: round(ms, 4) for st, ms in steps.items() if st != "attention"},
+              "note": "the two all-to-alls of q/k/v and o are not run on one GPU"}
+    print(json.dumps(result), flush=True)
+
+
 def bench_adapters(args):
     """The input and output adapters around the backbone at one workload:
     patchify and input projection of every interval into the packed
@@ -433,6 +515,8 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="time the eleven-call block (no fused epilogues)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the four projections as FP8 (e4m3) GEMMs with row-wise activation quantisation")
+    ap.add_argument("--shard", type=int, default=0,
+                    help="time one GPU's share of the block at this many GPUs (sequence parallel)")
     ap.add_argument("--fp8-block", action="store_true",
                     help="time the FP8 block (projections and attention on e4m3) beside the fused bf16 block")
     ap.add_argument("--fp8-attn", action="store_true",
@@ -457,6 +541,9 @@ def main():
     blk.load()
     if args.io:
         bench_adapters(args)
+        return
+    if args.shard:
+        bench_shard(args)
         return
     if args.fp8_block:
         bench_fp8_block(args)
