@@ -295,6 +295,49 @@ def bench_fp8_attention(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_fp8_stack(args):
+    """One sampling step of the 50-block stack with every block on FP8
+    operands (H3BlockFP8) and the Euler update; weights drawn on the device
+    block by block and quantised as they are made (about 19 GB of e4m3 codes
+    stay resident, the bf16 draws do not)."""
+    import torch
+
+    from video_audio_diffusion_amd import inputs
+    from video_audio_diffusion_amd.block import H3Stack, device_inputs, interleave_gate_up
+
+    scfg = inputs.STACKS[args.config]
+    cfg = scfg.block
+    log(f"fp8 stack {scfg.name}: {scfg.n_blocks} blocks, {cfg.n_tok} tokens; drawing and quantising weights")
+    x = device_inputs(cfg, inputs.make_inputs(cfg, ("x",)))["x"]
+    stack = H3Stack(scfg, (interleave_gate_up(device_block_weights(cfg, b), keep_plain=False)
+                           for b in range(scfg.n_blocks)), fp8=True)
+    torch.cuda.synchronize()
+    log(f"weights resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+    n_st = len(stack.block.steps)
+    for _ in range(args.warmup):
+        stack.forward(x)
+    torch.cuda.synchronize()
+    K_ = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(scfg.n_blocks)]
+          for _ in range(K_)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(K_)]
+    for i in range(K_):
+        stack.forward(x, block_events=ev[i])
+        end[i].record()
+    torch.cuda.synchronize()
+    total = ev[0][0][0].elapsed_time(end[-1]) / K_
+    per = {st: sum(ev[i][b][j].elapsed_time(ev[i][b][j + 1]) for i in range(K_) for b in range(scfg.n_blocks)) / K_
+           for j, st in enumerate(stack.block.steps)}
+    result = {"metric": "H3 50-block sampling step, FP8 (e4m3) projections and attention", "unit": "s",
+              "value": round(total / 1e3, 4), "n_gpus": 1, "steps": K_, "warmup": args.warmup,
+              "ms_per_step": round(total, 2), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+              "dtype": "fp8-e4m3 (fp32 sums, bf16 activations)", "data": "synthetic",
+              "config": {"workload": f"{scfg.name}", "blocks": scfg.n_blocks, "tokens": cfg.n_tok},
+              "tokens_per_s": round(cfg.n_tok / (total * 1e-3), 1),
+              "kernels_ms_summed_over_blocks": {st: round(ms, 2) for st, ms in per.items()}}
+    print(json.dumps(result), flush=True)
+
+
 def bench_fp8_block(args):
     """The FP8 variant of the block (H3BlockFP8: projections and attention on
     e4m3 operands, quantisation included) at one workload; the fused bf16
@@ -546,7 +589,10 @@ def main():
         bench_shard(args)
         return
     if args.fp8_block:
-        bench_fp8_block(args)
+        if args.config in inputs.STACKS:
+            bench_fp8_stack(args)
+        else:
+            bench_fp8_block(args)
         return
     if args.fp8_attn:
         bench_fp8_attention(args)

@@ -293,3 +293,47 @@ def test_768p15s_fp8_block_each_call():
     assert torch.equal(got, r["out"])
     rows = inputs.sample_rows(c, n_random=48)
     _check_calls(c, host, block, r, rows=rows, attn_heads=(0, 7, 13, 22, 31, 40, 47, 55))
+
+
+def test_small_fp8_stack():
+    """Four FP8 blocks and the Euler step at the ragged 117-token width-256
+    block: the stack's velocity equals the blocks run one after another (bit
+    for bit); the Euler update of the GPU's own velocity against the oracle
+    (bf16, 2e-2 on the delta beyond output rounding); and the stack's total
+    update v - x against the unquantised fp64 stack within the block bound,
+    since each block's quantisation error is its own."""
+    import torch
+    from video_audio_diffusion_amd.block import H3Stack
+    b = _small()
+    sc = inputs.StackConfig(name="stack4-ragged-bf16", block=b, n_blocks=4, description="fp8 stack parity")
+    blocks = [inputs.make_stack_block(b, i) for i in range(sc.n_blocks)]
+    x = inputs.make_inputs(b, ("x",))["x"]
+    weights = []
+    for t in blocks:
+        d = device_inputs(b, t)
+        weights.append(interleave_gate_up(BlockWeights(d["w_qkv"], d["w_o"], d["w_gu"], d["w_d"], d["mod"],
+                                                       d["gamma_q"], d["gamma_k"]), keep_plain=False))
+    stack = H3Stack(sc, weights, fp8=True)
+    xd = _dev(x)
+    stack.forward(xd)
+    v = stack.block.buf["out"].clone()
+    one = H3BlockFP8(b, stack.weights[0])
+    h = _dev(x)
+    for w in stack.weights:
+        h = one.forward(h, weights=w).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(v, h), "the stack differs from its blocks run one after another"
+    coef = np.zeros(b.n_tok)
+    for s, cv in zip(b.segments, stack.coef_values):
+        coef[s.start:s.start + s.length] = cv
+    x64, v64 = inputs.widen(x, "bf16"), widen(v, "bf16")
+    ref = oracle.euler_update(x64, v64, coef)
+    got = widen(xd, "bf16")
+    assert_close("fp8 stack euler", got, ref, TB)
+    assert_delta_close("fp8 stack euler delta", got, ref, x64, TB, "bf16")
+    t64 = [{k: inputs.widen(a, "bf16") if a.dtype == np.uint16 else a.astype(np.float64) for k, a in t.items()}
+           for t in blocks]
+    _, v_ref = oracle.stack_forward(x64, t64, b, sc.step, sc.n_steps, dict(sc.shifts))
+    e_f = np.linalg.norm((v64 - x64) - (v_ref - x64)) / np.linalg.norm(v_ref - x64)
+    print(f"  fp8 stack update vs unquantised: e_F={e_f:.3e} (tol {TOL_BLOCK:g})", flush=True)
+    assert e_f <= TOL_BLOCK

@@ -166,6 +166,27 @@ def quantize_rows_fp8(w, stream: Optional[int] = None):
     return q, sc
 
 
+@dataclass
+class FP8Weights:
+    """One block's weights for H3BlockFP8: e4m3 codes and fp32 per-output-
+    channel scales of W_qkv, W_o, the interleaved W_gu and W_d (keys qkv, o,
+    gu, d), plus the modulation table and the q/k gains as in BlockWeights."""
+    q: Dict[str, object]
+    mod: object
+    gamma_q: object = None
+    gamma_k: object = None
+
+
+def quantize_block_weights(weights: BlockWeights) -> FP8Weights:
+    """BlockWeights (with the interleaved gate/up copy) -> FP8Weights; a
+    one-time weight step on the device."""
+    if weights.w_gu_il is None:
+        raise ValueError("the FP8 block needs interleaved gate/up weights (interleave_gate_up)")
+    return FP8Weights({"qkv": quantize_rows_fp8(weights.w_qkv), "o": quantize_rows_fp8(weights.w_o),
+                       "gu": quantize_rows_fp8(weights.w_gu_il), "d": quantize_rows_fp8(weights.w_d)},
+                      weights.mod, weights.gamma_q, weights.gamma_k)
+
+
 class H3BlockFP8:
     """The block with its four projections and its attention on FP8 (OCP
     e4m3) operands -- the quantised variant of the fused block: every GEMM
@@ -180,18 +201,18 @@ class H3BlockFP8:
     STEPS = ("adaln_attn", "quant_a", "gemm_qkv", "qknorm_rope", "quant_qkv", "attention", "quant_o",
              "gemm_o_gate", "adaln_ffn", "quant_a2", "gemm_gu_swiglu", "quant_h", "gemm_d_gate")
 
-    def __init__(self, cfg, weights: BlockWeights, device="cuda"):
+    def __init__(self, cfg, weights, device="cuda"):
+        """`weights`: BlockWeights (quantised here) or FP8Weights."""
         import torch
         if cfg.dtype != "bf16" or cfg.head_dim != 128 or any(v % 128 for v in (cfg.dim, cfg.inner, cfg.ffn)):
             raise ValueError("the FP8 block takes bf16, head_dim 128 and widths that are multiples of 128")
-        if weights.w_gu_il is None:
-            raise ValueError("the FP8 block needs interleaved gate/up weights (interleave_gate_up)")
-        self.cfg, self.w = cfg, weights
+        self.cfg = cfg
+        self.w = weights if isinstance(weights, FP8Weights) else quantize_block_weights(weights)
+        self.wq = self.w.q
+        self.dt = blk.H3_BF16
         self.steps = self.STEPS
         N, D, I, F, H = cfg.n_tok, cfg.dim, cfg.inner, cfg.ffn, cfg.heads
         self.n_pad = -(-N // 64) * 64
-        self.wq = {"qkv": quantize_rows_fp8(weights.w_qkv), "o": quantize_rows_fp8(weights.w_o),
-                   "gu": quantize_rows_fp8(weights.w_gu_il), "d": quantize_rows_fp8(weights.w_d)}
         b16 = lambda *sh: torch.empty(*sh, dtype=torch.bfloat16, device=device)
         u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device=device)
         f32 = lambda *sh: torch.empty(*sh, dtype=torch.float32, device=device)
@@ -201,13 +222,16 @@ class H3BlockFP8:
             "sq": f32(H, N), "sk": f32(H), "sv": f32(H), "o8": u8(N, I), "so": f32(N), "h8": u8(N, F), "sh": f32(N)}
         self.segs = blk.segments(cfg.segments)
         self.n_segs = len(cfg.segments)
-        self.n_sets = int(weights.mod.shape[0])
+        self.n_sets = int(self.w.mod.shape[0])
 
-    def forward(self, x, stream: Optional[int] = None, events=None):
+    def forward(self, x, stream: Optional[int] = None, events=None, weights: Optional[FP8Weights] = None):
         """Run the block on x [N, D]; returns the `out` buffer (x may be it).
-        With `events` (len(STEPS) + 1 torch.cuda.Event), event i is recorded
-        before step i and the last after the final step."""
-        c, b, w, wq = self.cfg, self.buf, self.w, self.wq
+        `weights` replaces the block's own for this call.  With `events`
+        (len(STEPS) + 1 torch.cuda.Event), event i is recorded before step i
+        and the last after the final step."""
+        c, b = self.cfg, self.buf
+        w = self.w if weights is None else weights
+        wq = w.q
         N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
         segs, ns, nset = self.segs, self.n_segs, self.n_sets
         BF = blk.H3_BF16
@@ -283,13 +307,23 @@ class H3Stack:
     the last block's output, and h3_euler_update moves the target intervals
     of the input latent by the step's coefficients (sampler.py)."""
 
-    def __init__(self, stack_cfg, weights, device="cuda", fused: bool = False):
+    def __init__(self, stack_cfg, weights, device="cuda", fused: bool = False, fp8: bool = False):
+        """`weights`: one BlockWeights per block (interleaved gate/up copies
+        for the fused and FP8 blocks) or, with fp8, FP8Weights.  With fp8
+        every block is H3BlockFP8 and only the quantised weights are kept;
+        BlockWeights given here are quantised as they are taken, so a caller
+        that passes a generator never holds more than one block's bf16
+        weights."""
         from . import sampler
         self.cfg = stack_cfg
-        self.weights = list(weights)
+        if fp8:
+            self.weights = [w if isinstance(w, FP8Weights) else quantize_block_weights(w) for w in weights]
+        else:
+            self.weights = list(weights)
         if len(self.weights) != stack_cfg.n_blocks:
             raise ValueError(f"{len(self.weights)} weight sets for {stack_cfg.n_blocks} blocks")
-        self.block = H3Block(stack_cfg.block, self.weights[0], device, fused=fused)
+        self.block = (H3BlockFP8(stack_cfg.block, self.weights[0], device) if fp8 else
+                      H3Block(stack_cfg.block, self.weights[0], device, fused=fused))
         self.coef_values = sampler.step_coefficients(stack_cfg.block.segments, stack_cfg.step,
                                                      stack_cfg.n_steps, dict(stack_cfg.shifts))
         self.coef = blk.coefficients(self.coef_values)
