@@ -76,7 +76,8 @@ def step_flops(cfg):
     N, D, H, d, I, F = cfg.n_tok, cfg.dim, cfg.heads, cfg.head_dim, cfg.inner, cfg.ffn
     f = {"gemm_qkv": 2 * N * D * 3 * I, "attention": 4 * N * N * H * d, "gemm_o": 2 * N * I * D,
          "gemm_gu": 2 * N * D * 2 * F, "gemm_d": 2 * N * F * D}
-    f.update(gemm_o_gate=f["gemm_o"], gemm_gu_swiglu=f["gemm_gu"], gemm_d_gate=f["gemm_d"])
+    f.update(gemm_qkv_rope=f["gemm_qkv"], gemm_o_gate=f["gemm_o"], gemm_gu_swiglu=f["gemm_gu"],
+             gemm_d_gate=f["gemm_d"])
     return f
 
 

@@ -20,9 +20,11 @@
  *   f   = h3_gemm_bf16(h, W_d)                14336 -> 5376
  *   out = h3_gate_residual(x1, f, FFN)
  *
- * The fused entry points h3_gemm_gate_residual (output projection + gated
- * residual) and h3_gemm_swiglu (gate/up projection + SwiGLU) run the same
- * block in eight calls, without writing y, gu or f to memory.
+ * The fused entry points h3_gemm_qknorm_rope (QKV projection + per-head
+ * norm and RoPE of q and k), h3_gemm_gate_residual (output projection +
+ * gated residual) and h3_gemm_swiglu (gate/up projection + SwiGLU) run the
+ * same block in seven calls, without writing y, gu or f to memory or
+ * reading q and k back.
  *
  * Conventions shared by every call:
  *   - Tensors are row-major with tokens as rows.  Every pointer argument is
@@ -167,6 +169,31 @@ h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok,
                            int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
                            const h3_segment* segs, int32_t n_segs,
                            h3_dtype dt, void* stream);
+
+/* The QKV projection fused with h3_qknorm_rope3d ([notes] 3.2: q and k
+ * are normed per head before the positional encoding; [reading] 5 and 7.4
+ * for the 3-D RoPE):
+ *   C = A . W^T, then columns [0, heads*head_dim) (q heads) and
+ *   [heads*head_dim, 2*heads*head_dim) (k heads) are normed and rotated as
+ *   h3_qknorm_rope3d does; later columns (v) are stored as computed.
+ * The product is rounded to dt before the norm, so q and k are computed from
+ * the values h3_gemm_bf16 would store.  The angles are taken in fp32
+ * (revolutions reduced to [-1/2, 1/2], hardware sine and cosine), not in
+ * double as h3_qknorm_rope3d does: q and k may differ from that call's by a
+ * unit in the last place of dt.
+ *   A : [M][K] row stride lda;  W : [N][K] row stride ldw;  C : [M][N] row
+ *       stride ldc, must not overlap A or W
+ *   gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base, segs : as for
+ *       h3_qknorm_rope3d (segs cover [0, M))
+ * heads*head_dim a multiple of 256 and 2*heads*head_dim <= N; other shape
+ * rules of h3_gemm_bf16 and h3_qknorm_rope3d apply. */
+h3_status h3_gemm_qknorm_rope(const void* A, int64_t lda, const void* W, int64_t ldw,
+                              void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                              int32_t heads, int32_t head_dim,
+                              const float* gamma_q, const float* gamma_k, float eps,
+                              int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
+                              const h3_segment* segs, int32_t n_segs,
+                              h3_dtype dt, void* stream);
 
 /* Full bidirectional softmax attention per head ([notes] section 5: one
  * non-causal self-attention over all valid tokens, no mask):

@@ -149,6 +149,34 @@ def test_qknorm_rope_validation(lib):
     assert r(ns=2) == blk.H3_ERR_SEGMENTS
 
 
+def test_gemm_qknorm_rope_validation(lib):
+    L = blk.load()
+    A, W, C = P, P + (1 << 32), P + (2 << 32)
+    segs = blk.segments(CFG2.segments)
+    def g(**kw):
+        a = dict(A=A, lda=5376, W=W, ldw=5376, C=C, ldc=21504, M=CFG2.n_tok, N=21504, K=5376, heads=56, hd=128,
+                 gq=None, gk=None, eps=1e-6, dt_=64, dh=32, dw=32, base=1e4, segs=segs, ns=len(CFG2.segments), dt=0)
+        a.update(kw)
+        return L.h3_gemm_qknorm_rope(a["A"], a["lda"], a["W"], a["ldw"], a["C"], a["ldc"], a["M"], a["N"], a["K"],
+                                     a["heads"], a["hd"], a["gq"], a["gk"], a["eps"], a["dt_"], a["dh"], a["dw"],
+                                     a["base"], a["segs"], a["ns"], a["dt"], 0)
+    assert g(dt=2) == blk.H3_ERR_DTYPE
+    assert g(A=0) == blk.H3_ERR_ARG
+    assert g(ldc=100) == blk.H3_ERR_ARG
+    assert g(K=5376 - 8, lda=5368, ldw=5368) == blk.H3_ERR_SHAPE        # bf16 K % 64
+    assert g(C=A + 1024) == blk.H3_ERR_ARG                                # C overlaps A
+    assert g(heads=0) == blk.H3_ERR_ARG
+    assert g(eps=-1.0) == blk.H3_ERR_ARG
+    assert g(base=0.0) == blk.H3_ERR_ARG
+    assert g(hd=96) == blk.H3_ERR_SHAPE
+    assert g(dt_=63, dh=33) == blk.H3_ERR_SHAPE
+    assert g(heads=55) == blk.H3_ERR_SHAPE              # q heads do not fill whole 256-column tiles
+    assert g(heads=86) == blk.H3_ERR_SHAPE              # q and k need 22016 > N columns
+    assert g(gq=P + 2) == blk.H3_ERR_ALIGN
+    assert g(ns=2) == blk.H3_ERR_SEGMENTS
+    assert g(M=0, segs=None, ns=0) == blk.H3_OK         # nothing to do, nothing launched
+
+
 def test_attention_validation(lib):
     L = blk.load()
     q, k, v, o = P, P + 14336, P + 28672, P + (4 << 32)

@@ -28,6 +28,7 @@ def test_step_flops_match_the_workload():
     assert gemm / N == 2 * (5376 * 21504 + 7168 * 5376 + 5376 * 28672 + 14336 * 5376)
     assert f["attention"] == 4 * N * N * 56 * 128
     assert f["gemm_o_gate"] == f["gemm_o"] and f["gemm_gu_swiglu"] == f["gemm_gu"]
+    assert f["gemm_qkv_rope"] == f["gemm_qkv"]
 
 
 def test_step_bytes_of_the_streaming_passes():

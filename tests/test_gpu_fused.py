@@ -6,7 +6,8 @@
   bf16 and fp32.
 * h3_gemm_swiglu: SiLU(gate) * up from the 32-row interleaved weight, F
   below and above one 256-column tile, ragged M, bf16 and fp32.
-* The eight-call fused block: end to end at a ragged 117-token width-256
+* The seven-call fused block (QKV projection with q/k norm and RoPE in its
+  epilogue): end to end at a ragged 117-token width-256
   block, and at the 15 s 768p workload (92840 tokens, full width, the launch
   configuration the benchmark times) every call on sampled rows against the
   oracle applied to the GPU's own inputs to that call, attention over all

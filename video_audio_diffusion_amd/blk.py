@@ -24,7 +24,7 @@ EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
            "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
            "h3_gemm_fp8", "h3_gemm_fp8_gate_residual", "h3_gemm_fp8_swiglu", "h3_quantize_qkv_fp8",
-           "h3_attention_fp8")
+           "h3_attention_fp8", "h3_gemm_qknorm_rope")
 
 
 class H3Segment(ctypes.Structure):
@@ -52,6 +52,8 @@ _SIGS = {
     "h3_gemm_gate_residual": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _I32,
                               _P],
     "h3_gemm_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P],
+    "h3_gemm_qknorm_rope": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _F, _I32, _I32,
+                            _I32, _F, _P, _I32, _I32, _P],
     "h3_patchify": [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P],
     "h3_unpatchify": [_P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P],
     "h3_quantize_fp8": [_P, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
@@ -143,6 +145,14 @@ def h3_gemm_gate_residual(A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets, br,
 def h3_gemm_swiglu(A, lda, Wgu, ldw, H, ldh, M, F, K, dt, stream=None):
     _check("h3_gemm_swiglu", load().h3_gemm_swiglu(ptr(A), lda, ptr(Wgu), ldw, ptr(H), ldh, M, F, K, dt,
                                                    _stream(stream)))
+
+
+def h3_gemm_qknorm_rope(A, lda, W, ldw, C, ldc, M, N, K, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w,
+                        rope_base, segs, n_segs, dt, stream=None):
+    _check("h3_gemm_qknorm_rope",
+           load().h3_gemm_qknorm_rope(ptr(A), lda, ptr(W), ldw, ptr(C), ldc, M, N, K, heads, head_dim, ptr(gamma_q),
+                                      ptr(gamma_k), eps, d_t, d_h, d_w, rope_base, segs, n_segs, dt,
+                                      _stream(stream)))
 
 
 def h3_patchify(latent, T, H, W, C, pt, ph, pw, tokens, ld, dt, stream=None):

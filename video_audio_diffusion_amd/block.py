@@ -1,5 +1,5 @@
 """One H3-Omni-Transformer block forward as eleven libh3blk calls, as
-eight with the fused projection epilogues, or (H3BlockFP8) as thirteen with
+seven with the fused projection epilogues, or (H3BlockFP8) as thirteen with
 FP8 projections and attention.
 
 This driver only allocates device buffers (torch) and issues the calls in
@@ -16,8 +16,9 @@ Buffers (row-major, tokens as rows):
     gu  [N, 2F]   [gate | up]
     h   [N, F]    SwiGLU output
     out [N, D]
-The fused mode writes neither y nor gu: the output and down projections add
-their gated residual in the GEMM epilogue, and the gate/up projection (its
+The fused mode writes neither y nor gu and does not read q and k back: the
+QKV projection norms and rotates q and k in its epilogue, the output and down
+projections add their gated residual there, and the gate/up projection (its
 weight rows interleaved once, `interleave_gate_up`) applies SwiGLU there.
 """
 from __future__ import annotations
@@ -56,8 +57,8 @@ def interleave_gate_up(weights: BlockWeights, keep_plain: bool = True) -> BlockW
 class H3Block:
     STEPS = ("adaln_attn", "gemm_qkv", "qknorm_rope", "attention", "gemm_o", "gate_attn",
              "adaln_ffn", "gemm_gu", "swiglu", "gemm_d", "gate_ffn")
-    STEPS_FUSED = ("adaln_attn", "gemm_qkv", "qknorm_rope", "attention", "gemm_o_gate", "adaln_ffn",
-                   "gemm_gu_swiglu", "gemm_d_gate")
+    STEPS_FUSED = ("adaln_attn", "gemm_qkv_rope", "attention", "gemm_o_gate", "adaln_ffn", "gemm_gu_swiglu",
+                   "gemm_d_gate")
 
     def __init__(self, cfg, weights: BlockWeights, device="cuda", fused: bool = False):
         import torch
@@ -134,23 +135,21 @@ class H3Block:
         rec(0)
         blk.h3_adaln_modulate(x, b["a"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, c.eps, dt, st)
         rec(1)
-        blk.h3_gemm_bf16(b["a"], D, w.w_qkv, D, qkv, 3 * I, N, 3 * I, D, dt, st)
+        blk.h3_gemm_qknorm_rope(b["a"], D, w.w_qkv, D, qkv, 3 * I, N, 3 * I, D, H, d, w.gamma_q, w.gamma_k, c.eps,
+                                *c.rope_split, c.rope_base, segs, ns, dt, st)
         rec(2)
-        blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base,
-                             segs, ns, dt, st)
-        rec(3)
         blk.h3_attention_fwd(q, k, v, 3 * I, b["o"], I, N, H, d, c.scale, None, dt, st)
-        rec(4)
+        rec(3)
         blk.h3_gemm_gate_residual(b["o"], I, w.w_o, I, x, b["x1"], D, N, D, I, w.mod, nset, blk.H3_BRANCH_ATTN,
                                   segs, ns, dt, st)
-        rec(5)
+        rec(4)
         blk.h3_adaln_modulate(b["x1"], b["a"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, c.eps, dt, st)
-        rec(6)
+        rec(5)
         blk.h3_gemm_swiglu(b["a"], D, w.w_gu_il, D, b["h"], F, N, F, D, dt, st)
-        rec(7)
+        rec(6)
         blk.h3_gemm_gate_residual(b["h"], F, w.w_d, F, b["x1"], b["out"], D, N, D, F, w.mod, nset,
                                   blk.H3_BRANCH_FFN, segs, ns, dt, st)
-        rec(8)
+        rec(7)
         return b["out"]
 
 

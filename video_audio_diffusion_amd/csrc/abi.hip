@@ -76,6 +76,21 @@ h3_status check_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, con
 
 inline h3_status hip_status(hipError_t e) { return e == hipSuccess ? H3_OK : H3_ERR_HIP; }
 
+// Per-pair rotation table, exact in double: pair p of a head lies in the
+// t, h or w chunk (widths d_t, d_h, d_w, already checked to sum to
+// head_dim) and turns at base^(-2j/d_axis), j its index inside the chunk.
+void fill_rope(int32_t head_dim, int32_t d_t, int32_t d_h, int32_t d_w, float rope_base, RopeTable* rt) {
+    memset(rt, 0, sizeof(*rt));
+    const int split[3] = {d_t, d_h, d_w};
+    int axis = 0, first = 0;
+    for (int p = 0; p < head_dim / 2; ++p) {
+        while (2 * p >= first + split[axis]) first += split[axis++];
+        const int j = p - first / 2;
+        rt->axis[p] = (int8_t)axis;
+        rt->inv_freq[p] = pow((double)rope_base, -2.0 * j / (double)split[axis]);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,19 +191,36 @@ h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok, int32_t 
     const h3_status st = build_segs(segs, n_segs, n_tok, 0, &tab);
     if (st != H3_OK) return st;
     if (n_tok == 0) return H3_OK;
-    // per-pair rotation table, exact in double: frequency base^(-2j/d_axis)
     RopeTable rt;
-    memset(&rt, 0, sizeof(rt));
-    const int split[3] = {d_t, d_h, d_w};
-    int axis = 0, first = 0;
-    for (int p = 0; p < head_dim / 2; ++p) {
-        while (2 * p >= first + split[axis]) first += split[axis++];
-        const int j = p - first / 2;
-        rt.axis[p] = (int8_t)axis;
-        rt.inv_freq[p] = pow((double)rope_base, -2.0 * j / (double)split[axis]);
-    }
+    fill_rope(head_dim, d_t, d_h, d_w, rope_base, &rt);
     return hip_status(launch_qknorm_rope(dt == H3_BF16, q, k, ld, (int32_t)n_tok, heads, head_dim, gamma_q,
                                          gamma_k, eps, rt, tab, (hipStream_t)stream));
+}
+
+h3_status h3_gemm_qknorm_rope(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+                              int64_t M, int32_t N, int32_t K, int32_t heads, int32_t head_dim,
+                              const float* gamma_q, const float* gamma_k, float eps, int32_t d_t, int32_t d_h,
+                              int32_t d_w, float rope_base, const h3_segment* segs, int32_t n_segs, h3_dtype dt,
+                              void* stream) {
+    h3_status st = check_gemm(A, lda, W, ldw, C, ldc, M, N, K, N, dt);
+    if (st != H3_OK) return st;
+    if (heads < 1 || !(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base))
+        return H3_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
+    if (d_t < 0 || d_h < 0 || d_w < 0 || d_t % 2 || d_h % 2 || d_w % 2 || d_t + d_h + d_w != head_dim)
+        return H3_ERR_SHAPE;
+    // q and k heads fill whole 256-column tiles, and both fit in C's columns
+    const int64_t q_cols = (int64_t)heads * head_dim;
+    if (q_cols % 256 || 2 * q_cols > N) return H3_ERR_SHAPE;
+    if (((uintptr_t)gamma_q & 3) || ((uintptr_t)gamma_k & 3)) return H3_ERR_ALIGN;
+    SegTable tab;
+    st = build_segs(segs, n_segs, M, 0, &tab);
+    if (st != H3_OK) return st;
+    if (M == 0) return H3_OK;
+    RopeTable rt;
+    fill_rope(head_dim, d_t, d_h, d_w, rope_base, &rt);
+    return hip_status(launch_gemm_qknorm_rope(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, heads, head_dim,
+                                              gamma_q, gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
 
 h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o, int64_t ld_o,

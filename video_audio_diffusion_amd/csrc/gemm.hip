@@ -25,6 +25,7 @@
 // output: their A and W panels are then shared in that XCD's L2.
 #include "launch.h"
 
+#include <cstring>
 #include <type_traits>
 
 namespace h3 {
@@ -145,6 +146,34 @@ struct EpiGate {
     SegTable tab;
 };
 struct EpiSwiglu {};
+// EpiQkRope: the QKV projection with the per-head RMSNorm and the 3-D RoPE
+// of q and k applied before the store.  Columns [0, q_cols) are q heads and
+// [q_cols, 2 q_cols) k heads, HD wide; later columns (v) are stored as
+// computed.  q_cols is a multiple of the 256-column tile, so a tile is all
+// q, all k or all v.  A q or k tile is first rounded to the output type into
+// LDS -- the values a separate norm pass would read back from memory --
+// then each (row, head) is scaled by 1 / sqrt(mean square + eps) and the gain,
+// and pair p (elements 2p, 2p+1 of a head) turns by fr[p] * pos revolutions,
+// pos being the row's position on axis[p].  fr is held as two floats and
+// the product reduced to about [-1/2, 1/2] revolutions with an fma, so the
+// angle keeps about 2^-40 revolutions of precision at any position (a plain
+// fp32 product loses 2^-24 of pos * fr: 1e-4 rad at position 5000); sine and
+// cosine are the hardware's for bf16 output and the precise sincospif for
+// fp32.
+template <int HD>
+struct EpiQkRope {
+    static constexpr int kHd = HD;
+    const float* gq;        // [HD] gain of the q heads (null: 1)
+    const float* gk;        // [HD] gain of the k heads
+    float eps;
+    int32_t q_cols;         // heads * HD
+    float fr_hi[HD / 2];    // revolutions per unit of position of pair p,
+    float fr_lo[HD / 2];    //   as an fp32 pair: fr_hi + fr_lo
+    int8_t axis[HD / 2];    // 0 = t, 1 = h, 2 = w
+    SegTable tab;
+};
+template <typename E> struct IsQkRope : std::false_type {};
+template <int HD> struct IsQkRope<EpiQkRope<HD>> : std::true_type {};
 
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
 // the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
@@ -324,7 +353,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                 for (int j = 0; j < NJ; ++j) acc[i][j][r] *= rs * cs[j];
             }
     }
-    if constexpr (std::is_same<EPI, EpiStore>::value) {
+    // plain store of the accumulators (rows and columns past M, N skipped)
+    auto store_c = [&]() __attribute__((always_inline)) {
         T* cbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
         if (full) {
 #pragma unroll
@@ -350,6 +380,9 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                     }
                 }
         }
+    };
+    if constexpr (std::is_same<EPI, EpiStore>::value) {
+        store_c();
     } else if constexpr (std::is_same<EPI, EpiGate>::value) {
         const T* xb = reinterpret_cast<const T*>(epi.x);
         // One interval usually covers the whole tile: then every row takes the
@@ -405,6 +438,128 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                         GemmMfma<T>::store(C + o, GemmMfma<T>::load(xb + o) + gate(row, j) * acc[i][j][r]);
                     }
                 }
+        }
+    } else if constexpr (IsQkRope<EPI>::value) {
+        if (n0 >= 2 * epi.q_cols) {
+            store_c();    // a v tile
+        } else {
+            // The ring is reused as RPASS rows of the tile in T (16-byte chunk
+            // c of row r at slot c ^ (r % CPR)): all 256 rows for bf16, two
+            // passes of 128 for fp32.  The kernel declares no LDS beyond the
+            // ring: an allocation above 128 KB per workgroup was measured to
+            // slow the main loop by a sixth.  The CPH lanes that hold one row
+            // of a head (consecutive lanes, one 16-byte chunk each) sum its
+            // squares with a butterfly, so no per-row table is kept.
+            constexpr int HD = EPI::kHd;
+            constexpr int TB = (int)sizeof(T);
+            constexpr int RING = STAGES * 2 * TILE;
+            constexpr int RPASS = RING / (kBN * TB) < kBM ? RING / (kBN * TB) : kBM;
+            constexpr int CPR = kBN * TB / 16;        // 16-byte chunks per tile row
+            constexpr int VN = 16 / TB;               // values per chunk
+            constexpr int CPH = HD / VN;              // chunks (lanes) per row of a head
+            constexpr int HPT = kBN / HD;             // heads per tile
+            constexpr int NT = NWAVES * 64;
+            constexpr int RSTEP = NT / CPH;           // rows between a thread's rows
+            constexpr int RPT = RPASS / RSTEP;        // rows per thread and pass
+            static_assert(CPH <= 64 && NT % CPH == 0 && RPASS % RSTEP == 0 && kBM % RPASS == 0, "epilogue split");
+            auto chunk_at = [&](int rl, int ch) __attribute__((always_inline)) -> char* {
+                return ring + rl * (CPR * 16) + ((ch ^ (rl % CPR)) << 4);
+            };
+            const float* gam = n0 < epi.q_cols ? epi.gq : epi.gk;
+            // a thread always takes chunk cp of its rows: its pairs' gains,
+            // frequencies and axes are loaded once
+            const int cp = tid % CPH, d0 = cp * VN, r0 = tid / CPH;
+            float g[VN], frh[VN / 2], frl[VN / 2];
+            int ax[VN / 2];
+#pragma unroll
+            for (int e = 0; e < VN; ++e) g[e] = gam ? gam[d0 + e] : 1.0f;
+#pragma unroll
+            for (int e = 0; e < VN / 2; ++e) {
+                const int p = d0 / 2 + e;
+                frh[e] = epi.fr_hi[p];
+                frl[e] = epi.fr_lo[p];
+                ax[e] = epi.axis[p];
+            }
+#pragma unroll
+            for (int pass = 0; pass < kBM / RPASS; ++pass) {
+                // positions of this thread's rows (loads in flight during step 1)
+                int pt[RPT], ph[RPT], pw[RPT];
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) {
+                    const int row = m0 + pass * RPASS + r0 + k * RSTEP;
+                    pt[k] = ph[k] = pw[k] = 0;
+                    if (row < M) {
+                        const SegDev& sg = epi.tab.s[find_seg(epi.tab, row)];
+                        const int l = row - sg.start;
+                        pt[k] = sg.t0 + l / sg.HW;
+                        ph[k] = sg.h0 + (l / sg.W) % sg.H;
+                        pw[k] = sg.w0 + l % sg.W;
+                    }
+                }
+                // 1. this pass's rows, rounded to T (a 32-row block of a
+                //    wavefront lies in one pass); pass 0 first waits until
+                //    every wavefront's fragment reads are done
+                if (pass == 0) __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if ((wm * 128 + i * 32) / RPASS != pass) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int col = wn * NJ * 32 + j * 32 + frow;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int rl = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3) - pass * RPASS;
+                            reinterpret_cast<T*>(chunk_at(rl, col / VN))[col % VN] = (T)acc[i][j][r];
+                        }
+                    }
+                }
+                __syncthreads();
+                // 2. per row: the angles of the thread's pairs, then per head
+                //    the 1/rms (butterfly over the row's CPH lanes), gain,
+                //    rotation and store.  Every lane runs the butterfly;
+                //    rows past M only skip the store.
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) {
+                    const int rl = r0 + k * RSTEP;
+                    const int row = m0 + pass * RPASS + rl;
+                    float cs[VN / 2], sn[VN / 2];
+#pragma unroll
+                    for (int e = 0; e < VN / 2; ++e) {
+                        // pos * fr - (whole turns): the fma subtracts the turns from
+                        // the exact product pos * fr_hi, so the reduction is exact
+                        // whether or not the compiler contracts the sum after it
+                        const float pos = (float)(ax[e] == 0 ? pt[k] : ax[e] == 1 ? ph[k] : pw[k]);
+                        const float turns = __builtin_rintf(pos * frh[e]);
+                        const float x = __builtin_fmaf(pos, frh[e], -turns) + pos * frl[e];
+                        if constexpr (TB == 4) {
+                            sincospif(2.0f * x, &sn[e], &cs[e]);
+                        } else {
+                            sn[e] = __builtin_amdgcn_sinf(x);          // v_sin / v_cos take revolutions
+                            cs[e] = __builtin_amdgcn_cosf(x);
+                        }
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < HPT; ++hh) {
+                        float f[VN];
+                        Vec<T>::load(chunk_at(rl, hh * CPH + cp), f);
+                        float ss = 0.f;
+#pragma unroll
+                        for (int e = 0; e < VN; ++e) ss += f[e] * f[e];
+                        ss = sum_lanes<CPH>(ss);
+                        const float rstd = 1.0f / __builtin_sqrtf(ss / (float)HD + epi.eps);
+#pragma unroll
+                        for (int e = 0; e < VN; ++e) f[e] *= rstd * g[e];
+#pragma unroll
+                        for (int e = 0; e < VN; e += 2) {
+                            const float u0 = f[e], u1 = f[e + 1];
+                            f[e] = u0 * cs[e >> 1] - u1 * sn[e >> 1];
+                            f[e + 1] = u0 * sn[e >> 1] + u1 * cs[e >> 1];
+                        }
+                        if (row < M) Vec<T>::store(C + (int64_t)row * ldc + n0 + hh * HD + d0, f);
+                    }
+                }
+                if (pass + 1 < kBM / RPASS) __syncthreads();   // the next pass rewrites the tile
+            }
         }
     } else {
         static_assert(std::is_same<EPI, EpiSwiglu>::value && NJ == 2, "SwiGLU pairs a wavefront's two blocks");
@@ -497,6 +652,35 @@ hipError_t launch_gemm_gate(bool bf, const void* A, int64_t lda, const void* W, 
 hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* Wgu, int64_t ldw, void* H,
                               int64_t ldh, int64_t M, int32_t F, int32_t K, hipStream_t st) {
     return launch_gemm_epi(bf, A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, EpiSwiglu{}, st);
+}
+
+template <int HD>
+static hipError_t launch_qkrope_hd(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                                   int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t heads, const float* gq,
+                                   const float* gk, float eps, const RopeTable& rt, const SegTable& tab,
+                                   hipStream_t st) {
+    EpiQkRope<HD> e;
+    memset(&e, 0, sizeof(e));
+    e.gq = gq;
+    e.gk = gk;
+    e.eps = eps;
+    e.q_cols = heads * HD;
+    for (int p = 0; p < HD / 2; ++p) {
+        const double fr = rt.inv_freq[p] / (2.0 * 3.14159265358979323846);
+        e.fr_hi[p] = (float)fr;
+        e.fr_lo[p] = (float)(fr - (double)e.fr_hi[p]);
+        e.axis[p] = rt.axis[p];
+    }
+    e.tab = tab;
+    return launch_gemm_epi(bf, A, lda, W, ldw, C, ldc, M, N, K, e, st);
+}
+
+hipError_t launch_gemm_qknorm_rope(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                                  int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t heads, int32_t hd,
+                                  const float* gq, const float* gk, float eps, const RopeTable& rt,
+                                  const SegTable& tab, hipStream_t st) {
+    return hd == 128 ? launch_qkrope_hd<128>(bf, A, lda, W, ldw, C, ldc, M, N, K, heads, gq, gk, eps, rt, tab, st)
+                     : launch_qkrope_hd<64>(bf, A, lda, W, ldw, C, ldc, M, N, K, heads, gq, gk, eps, rt, tab, st);
 }
 
 hipError_t launch_gemm_fp8_gate(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,

@@ -30,6 +30,10 @@ hipError_t launch_gemm_gate(bool bf, const void* A, int64_t lda, const void* W, 
                             int32_t n_sets, int32_t br, const SegTable& tab, hipStream_t st);
 hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* Wgu, int64_t ldw, void* H,
                               int64_t ldh, int64_t M, int32_t F, int32_t K, hipStream_t st);
+hipError_t launch_gemm_qknorm_rope(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                                  int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t heads, int32_t hd,
+                                  const float* gq, const float* gk, float eps, const RopeTable& rt,
+                                  const SegTable& tab, hipStream_t st);
 // Latent grid [T][H][W][C] and its (pt, ph, pw) patch.
 struct PatchGeom {
     int32_t T, H, W, C, pt, ph, pw;
