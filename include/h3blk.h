@@ -311,6 +311,19 @@ h3_status h3_gemm_fp8_swiglu(const void* A, int64_t lda, const float* a_scale, c
                              int64_t ldw, const float* w_scale, void* H, int64_t ldh, int64_t M,
                              int32_t F, int32_t K, void* stream);
 
+/* The FP8 QKV projection fused with the per-head norm and RoPE of q and k
+ * (h3_gemm_qknorm_rope on e4m3 operands): C = diag(a_scale) (A . W^T)
+ * diag(w_scale) as h3_gemm_fp8 computes it, rounded to bf16, then q and k
+ * normed and rotated as h3_gemm_qknorm_rope does.  C is bf16.  Shape and
+ * layout rules of h3_gemm_fp8 and the head rules of h3_gemm_qknorm_rope
+ * apply. */
+h3_status h3_gemm_fp8_qknorm_rope(const void* A, int64_t lda, const float* a_scale, const void* W,
+                                  int64_t ldw, const float* w_scale, void* C, int64_t ldc, int64_t M,
+                                  int32_t N, int32_t K, int32_t heads, int32_t head_dim,
+                                  const float* gamma_q, const float* gamma_k, float eps,
+                                  int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
+                                  const h3_segment* segs, int32_t n_segs, void* stream);
+
 /* FP8 attention operands (same e4m3 format and rounding as h3_quantize_fp8;
  * [notes] section 5 defines the attention, [commentary] the FP8 practice):
  *   sq[h, i] = max_d |q[i, h, d]| / 448            (one scale per token and head)

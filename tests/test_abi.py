@@ -177,6 +177,28 @@ def test_gemm_qknorm_rope_validation(lib):
     assert g(M=0, segs=None, ns=0) == blk.H3_OK         # nothing to do, nothing launched
 
 
+def test_gemm_fp8_qknorm_rope_validation(lib):
+    L = blk.load()
+    A, sa, W, sw, C = P, P + (1 << 31), P + (1 << 32), P + (3 << 31), P + (2 << 32)
+    segs = blk.segments(CFG2.segments)
+    def g(**kw):
+        a = dict(A=A, lda=5376, sa=sa, W=W, ldw=5376, sw=sw, C=C, ldc=21504, M=CFG2.n_tok, N=21504, K=5376,
+                 heads=56, hd=128, gq=None, gk=None, eps=1e-6, dt_=64, dh=32, dw=32, base=1e4, segs=segs,
+                 ns=len(CFG2.segments))
+        a.update(kw)
+        return L.h3_gemm_fp8_qknorm_rope(a["A"], a["lda"], a["sa"], a["W"], a["ldw"], a["sw"], a["C"], a["ldc"],
+                                         a["M"], a["N"], a["K"], a["heads"], a["hd"], a["gq"], a["gk"], a["eps"],
+                                         a["dt_"], a["dh"], a["dw"], a["base"], a["segs"], a["ns"], 0)
+    assert g(sa=0) == blk.H3_ERR_ARG
+    assert g(K=5376 - 64, lda=5312, ldw=5312) == blk.H3_ERR_SHAPE      # fp8 K % 128
+    assert g(heads=55) == blk.H3_ERR_SHAPE
+    assert g(hd=96) == blk.H3_ERR_SHAPE
+    assert g(base=-1.0) == blk.H3_ERR_ARG
+    assert g(gk=P + 1) == blk.H3_ERR_ALIGN
+    assert g(ns=1) == blk.H3_ERR_SEGMENTS
+    assert g(M=0, segs=None, ns=0) == blk.H3_OK
+
+
 def test_attention_validation(lib):
     L = blk.load()
     q, k, v, o = P, P + 14336, P + 28672, P + (4 << 32)

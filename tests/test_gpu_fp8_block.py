@@ -7,7 +7,7 @@ projections against the oracle.
   then one bf16 rounding): 4e-3 on the output, and on the branch delta
   beyond the output's own rounding; ragged shapes, several intervals, in
   place.
-* The thirteen calls of the block replayed with a buffer per intermediate
+* The twelve calls of the block replayed with a buffer per intermediate
   (the driver's output must equal the replay bit for bit), each call
   against the oracle on the GPU's own inputs to it with that call's bound:
   quantisers bit for bit, fp8 products 4e-3, the fp8 attention 2^-4 (see
@@ -114,8 +114,9 @@ def _block(cfg, dev):
 
 
 def _replay(cfg, block, x):
-    """The block's thirteen calls with a separate buffer per intermediate
-    (qkv_raw is the QKV product before the in-place norm and rotation)."""
+    """The block's twelve calls with a separate buffer per intermediate
+    (qkv_raw is the plain QKV product of the same codes, h3_gemm_fp8, which
+    the fused call norms and rotates in its epilogue)."""
     import torch
     c, w, wq = cfg, block.w, block.wq
     N, D, H, d, I, F = c.n_tok, c.dim, c.heads, c.head_dim, c.inner, c.ffn
@@ -131,10 +132,12 @@ def _replay(cfg, block, x):
              sv=torch.empty(H, dtype=torch.float32, device="cuda"))
     blk.h3_adaln_modulate(x, r["a"], N, D, w.mod, nset, blk.H3_BRANCH_ATTN, segs, ns, c.eps, BF)
     r["a8"], r["sa"] = _quant(r["a"], D)
-    blk.h3_gemm_fp8(r["a8"], D, r["sa"], wq["qkv"][0], D, wq["qkv"][1], r["qkv"], 3 * I, N, 3 * I, D, BF)
-    r["qkv_raw"] = r["qkv"].clone()
+    # the plain product as well, for the GEMM's own check
+    r["qkv_raw"] = b16(N, 3 * I)
+    blk.h3_gemm_fp8(r["a8"], D, r["sa"], wq["qkv"][0], D, wq["qkv"][1], r["qkv_raw"], 3 * I, N, 3 * I, D, BF)
+    blk.h3_gemm_fp8_qknorm_rope(r["a8"], D, r["sa"], wq["qkv"][0], D, wq["qkv"][1], r["qkv"], 3 * I, N, 3 * I, D, H, d,
+                                w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base, segs, ns)
     q, k, v = r["qkv"][:, :I], r["qkv"][:, I:2 * I], r["qkv"][:, 2 * I:]
-    blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base, segs, ns, BF)
     blk.h3_quantize_qkv_fp8(q, k, v, 3 * I, N, H, d, r["q8"], r["k8"], r["vt"], n_pad, r["sq"], r["sk"], r["sv"], BF)
     blk.h3_attention_fp8(r["q8"], r["k8"], r["vt"], n_pad, r["sq"], r["sk"], r["sv"], r["o"], I, N, H, d, c.scale)
     r["o8"], r["so"] = _quant(r["o"], I)
@@ -182,10 +185,12 @@ def _check_calls(cfg, host, block, r, rows=None, attn_heads=None):
     assert np.array_equal(_host_rows(r["a8"], rows), qa) and np.array_equal(_host_rows(r["sa"], rows), sa)
     raw = _b16(r["qkv_raw"], rows)
     assert_close("gemm_fp8_qkv", raw, oracle.gemm_fp8(qa, sa, *wq["qkv"]), T8)
+    assert np.array_equal(host_array(_select(r["qkv"], rows), "bf16")[:, 2 * I:],
+                          host_array(_select(r["qkv_raw"], rows), "bf16")[:, 2 * I:]), "v differs from the plain product"
     qkv = _b16(r["qkv"], rows)
     for name, sl, gam in (("q", slice(0, I), t["gamma_q"]), ("k", slice(I, 2 * I), t["gamma_k"])):
         ref = oracle.rope3d(oracle.qk_rmsnorm(raw[:, sl], H, d, gam, c.eps), pos[R], H, d, c.rope_split, c.rope_base)
-        assert_close("qknorm_rope_" + name, qkv[:, sl], ref, TB)
+        assert_close("gemm_fp8_qknorm_rope_" + name, qkv[:, sl], ref, TB)
 
     # q/k/v codes: per-token q codes and scales on the rows; k and v with the
     # whole sequence's per-head scales

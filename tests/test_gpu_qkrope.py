@@ -11,7 +11,10 @@ RMSNorm and 3-D RoPE of q and k applied in its epilogue.
 * bf16 and fp32 (whose tile takes the epilogue in two passes), head_dim 128
   and 64, ragged M, a padded row stride, 8 v columns (N not a multiple of
   the tile), one interval or text + audio + video grids with position
-  offsets up to 5000, with and without gains.
+  offsets up to 5000, with and without gains;
+* h3_gemm_fp8_qknorm_rope (the same epilogue after the e4m3 product) against
+  h3_gemm_fp8 followed by h3_qknorm_rope3d, and q and k against the oracle's
+  norm and rotation of the oracle's product of the same codes.
 """
 import numpy as np
 import pytest
@@ -129,3 +132,57 @@ def test_gemm_qknorm_rope_no_tokens():
                             blk.H3_BF16)
     torch.cuda.synchronize()
     assert torch.count_nonzero(C) == 0
+
+
+def _ulp_check(name, got, two):
+    """Within one bf16 unit in the last place of the larger magnitude."""
+    diff = np.abs(got - two)
+    big = np.maximum(np.abs(got), np.abs(two))
+    bound = np.ldexp(1.0, np.frexp(big)[1] - 8) + 1e-5 * np.max(big)
+    print(f"  {name} vs two calls: max |diff| {diff.max():.3e}, identical {np.mean(diff == 0):.4f}", flush=True)
+    assert float(np.max(diff - bound)) <= 0, f"{name}: fused and two-call results differ by more than an ulp"
+
+
+@pytest.mark.parametrize("M,heads,hd,K,gains", [(300, 2, 128, 256, True), (513, 4, 64, 128, False),
+                                                 (1100, 6, 128, 384, True)])
+def test_gemm_fp8_qknorm_rope(M, heads, hd, K, gains):
+    import torch
+    qc = heads * hd
+    N = 3 * qc
+    split, base, eps = SPLIT[hd], 1e4, 1e-6
+    a = _dev(inputs.draw_rows(None, (M, K), 71 + M, dtype="bf16"))
+    w = _dev(inputs.draw_rows(None, (N, K), 72 + N, dtype="bf16"))
+    rng = np.random.Generator(np.random.PCG64(73))
+    gq = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32) if gains else None
+    gk = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32) if gains else None
+    gqd = _dev(gq) if gains else None
+    gkd = _dev(gk) if gains else None
+    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda")
+    qw = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda")
+    blk.h3_quantize_fp8(a, K, M, K, qa, K, sa, blk.H3_BF16)
+    blk.h3_quantize_fp8(w, K, N, K, qw, K, sw, blk.H3_BF16)
+    segs = _segments(M, "mixed")
+    hs = blk.segments(segs)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    print(f"[qkrope fp8] M={M} heads={heads} hd={hd} K={K}", flush=True)
+    blk.h3_gemm_fp8_qknorm_rope(qa, K, sa, qw, K, sw, C, N, M, N, K, heads, hd, gqd, gkd, eps, *split, base, hs,
+                                len(segs))
+    blk.h3_gemm_fp8(qa, K, sa, qw, K, sw, C2, N, M, N, K, blk.H3_BF16)
+    torch.cuda.synchronize()
+    plain = host_array(C2, "bf16")
+    blk.h3_qknorm_rope3d(C2[:, :qc], C2[:, qc:2 * qc], N, M, heads, hd, gqd, gkd, eps, *split, base, hs, len(segs),
+                         blk.H3_BF16)
+    torch.cuda.synchronize()
+    got_h = host_array(C, "bf16")
+    got, two = inputs.widen(got_h, "bf16"), inputs.widen(host_array(C2, "bf16"), "bf16")
+    assert np.array_equal(got_h[:, 2 * qc:], plain[:, 2 * qc:]), "v columns differ from h3_gemm_fp8"
+    raw = oracle.gemm_fp8(qa.cpu().numpy(), sa.cpu().numpy(), qw.cpu().numpy(), sw.cpu().numpy())
+    _, pos = oracle.token_table(segs, M)
+    for name, sl, gam in (("q", slice(0, qc), gq), ("k", slice(qc, 2 * qc), gk)):
+        g64 = np.ones(hd) if gam is None else gam.astype(np.float64)
+        ref = oracle.rope3d(oracle.qk_rmsnorm(raw[:, sl], heads, hd, g64, eps), pos, heads, hd, split, base)
+        assert_close(f"gemm_fp8_qknorm_rope {name} {M}x{N}x{K}", got[:, sl], ref, TOL["bf16"])
+        _ulp_check(name, got[:, sl], two[:, sl])

@@ -24,7 +24,7 @@ EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
            "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
            "h3_gemm_fp8", "h3_gemm_fp8_gate_residual", "h3_gemm_fp8_swiglu", "h3_quantize_qkv_fp8",
-           "h3_attention_fp8", "h3_gemm_qknorm_rope")
+           "h3_attention_fp8", "h3_gemm_qknorm_rope", "h3_gemm_fp8_qknorm_rope")
 
 
 class H3Segment(ctypes.Structure):
@@ -61,6 +61,8 @@ _SIGS = {
     "h3_gemm_fp8_gate_residual": [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P,
                                   _I32, _P],
     "h3_gemm_fp8_swiglu": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P],
+    "h3_gemm_fp8_qknorm_rope": [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _F,
+                                _I32, _I32, _I32, _F, _P, _I32, _P],
     "h3_quantize_qkv_fp8": [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _I64, _P, _P, _P, _I32, _P],
     "h3_attention_fp8": [_P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _F, _P],
 }
@@ -185,6 +187,14 @@ def h3_gemm_fp8_gate_residual(A, lda, a_scale, W, ldw, w_scale, x, out, ldo, M, 
 def h3_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K, stream=None):
     _check("h3_gemm_fp8_swiglu", load().h3_gemm_fp8_swiglu(ptr(A), lda, ptr(a_scale), ptr(Wgu), ldw, ptr(w_scale),
                                                            ptr(H), ldh, M, F, K, _stream(stream)))
+
+
+def h3_gemm_fp8_qknorm_rope(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, heads, head_dim, gamma_q, gamma_k,
+                            eps, d_t, d_h, d_w, rope_base, segs, n_segs, stream=None):
+    _check("h3_gemm_fp8_qknorm_rope",
+           load().h3_gemm_fp8_qknorm_rope(ptr(A), lda, ptr(a_scale), ptr(W), ldw, ptr(w_scale), ptr(C), ldc, M, N, K,
+                                          heads, head_dim, ptr(gamma_q), ptr(gamma_k), eps, d_t, d_h, d_w, rope_base,
+                                          segs, n_segs, _stream(stream)))
 
 
 def h3_quantize_qkv_fp8(q, k, v, ld, n_tok, heads, head_dim, q8, k8, vt, n_pad, sq, sk, sv, dt, stream=None):

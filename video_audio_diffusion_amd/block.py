@@ -1,5 +1,5 @@
 """One H3-Omni-Transformer block forward as eleven libh3blk calls, as
-seven with the fused projection epilogues, or (H3BlockFP8) as thirteen with
+seven with the fused projection epilogues, or (H3BlockFP8) as twelve with
 FP8 projections and attention.
 
 This driver only allocates device buffers (torch) and issues the calls in
@@ -197,8 +197,8 @@ class H3BlockFP8:
     vt, sq, sk, sv (attention operands), o8/so, h8/sh.  bf16, head_dim 128,
     D, I and F multiples of 128."""
 
-    STEPS = ("adaln_attn", "quant_a", "gemm_qkv", "qknorm_rope", "quant_qkv", "attention", "quant_o",
-             "gemm_o_gate", "adaln_ffn", "quant_a2", "gemm_gu_swiglu", "quant_h", "gemm_d_gate")
+    STEPS = ("adaln_attn", "quant_a", "gemm_qkv_rope", "quant_qkv", "attention", "quant_o", "gemm_o_gate",
+             "adaln_ffn", "quant_a2", "gemm_gu_swiglu", "quant_h", "gemm_d_gate")
 
     def __init__(self, cfg, weights, device="cuda"):
         """`weights`: BlockWeights (quantised here) or FP8Weights."""
@@ -244,33 +244,31 @@ class H3BlockFP8:
         rec(1)
         blk.h3_quantize_fp8(b["a"], D, N, D, b["a8"], D, b["sa"], BF, st)
         rec(2)
-        blk.h3_gemm_fp8(b["a8"], D, b["sa"], wq["qkv"][0], D, wq["qkv"][1], qkv, 3 * I, N, 3 * I, D, BF, st)
+        blk.h3_gemm_fp8_qknorm_rope(b["a8"], D, b["sa"], wq["qkv"][0], D, wq["qkv"][1], qkv, 3 * I, N, 3 * I, D, H, d,
+                                    w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base, segs, ns, st)
         rec(3)
-        blk.h3_qknorm_rope3d(q, k, 3 * I, N, H, d, w.gamma_q, w.gamma_k, c.eps, *c.rope_split, c.rope_base,
-                             segs, ns, BF, st)
-        rec(4)
         blk.h3_quantize_qkv_fp8(q, k, v, 3 * I, N, H, d, b["q8"], b["k8"], b["vt"], self.n_pad, b["sq"], b["sk"],
                                 b["sv"], BF, st)
-        rec(5)
+        rec(4)
         blk.h3_attention_fp8(b["q8"], b["k8"], b["vt"], self.n_pad, b["sq"], b["sk"], b["sv"], b["o"], I, N, H, d,
                              c.scale, st)
-        rec(6)
+        rec(5)
         blk.h3_quantize_fp8(b["o"], I, N, I, b["o8"], I, b["so"], BF, st)
-        rec(7)
+        rec(6)
         blk.h3_gemm_fp8_gate_residual(b["o8"], I, b["so"], wq["o"][0], I, wq["o"][1], x, b["x1"], D, N, D, I, w.mod,
                                       nset, blk.H3_BRANCH_ATTN, segs, ns, st)
-        rec(8)
+        rec(7)
         blk.h3_adaln_modulate(b["x1"], b["a"], N, D, w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, c.eps, BF, st)
-        rec(9)
+        rec(8)
         blk.h3_quantize_fp8(b["a"], D, N, D, b["a8"], D, b["sa"], BF, st)
-        rec(10)
+        rec(9)
         blk.h3_gemm_fp8_swiglu(b["a8"], D, b["sa"], wq["gu"][0], D, wq["gu"][1], b["h"], F, N, F, D, st)
-        rec(11)
+        rec(10)
         blk.h3_quantize_fp8(b["h"], F, N, F, b["h8"], F, b["sh"], BF, st)
-        rec(12)
+        rec(11)
         blk.h3_gemm_fp8_gate_residual(b["h8"], F, b["sh"], wq["d"][0], F, wq["d"][1], b["x1"], b["out"], D, N, D, F,
                                       w.mod, nset, blk.H3_BRANCH_FFN, segs, ns, st)
-        rec(13)
+        rec(12)
         return b["out"]
 
 

@@ -91,6 +91,27 @@ void fill_rope(int32_t head_dim, int32_t d_t, int32_t d_h, int32_t d_w, float ro
     }
 }
 
+// Checks of the q/k norm and rotation fused into a QKV projection of N
+// columns (after the GEMM's own checks); fills the interval and rotation
+// tables.
+h3_status check_qkrope(int64_t M, int32_t N, int32_t heads, int32_t head_dim, const float* gamma_q,
+                       const float* gamma_k, float eps, int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
+                       const h3_segment* segs, int32_t n_segs, SegTable* tab, RopeTable* rt) {
+    if (heads < 1 || !(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base))
+        return H3_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
+    if (d_t < 0 || d_h < 0 || d_w < 0 || d_t % 2 || d_h % 2 || d_w % 2 || d_t + d_h + d_w != head_dim)
+        return H3_ERR_SHAPE;
+    // q and k heads fill whole 256-column tiles, and both fit in C's columns
+    const int64_t q_cols = (int64_t)heads * head_dim;
+    if (q_cols % 256 || 2 * q_cols > N) return H3_ERR_SHAPE;
+    if (((uintptr_t)gamma_q & 3) || ((uintptr_t)gamma_k & 3)) return H3_ERR_ALIGN;
+    const h3_status st = build_segs(segs, n_segs, M, 0, tab);
+    if (st != H3_OK) return st;
+    fill_rope(head_dim, d_t, d_h, d_w, rope_base, rt);
+    return H3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,21 +225,10 @@ h3_status h3_gemm_qknorm_rope(const void* A, int64_t lda, const void* W, int64_t
                               void* stream) {
     h3_status st = check_gemm(A, lda, W, ldw, C, ldc, M, N, K, N, dt);
     if (st != H3_OK) return st;
-    if (heads < 1 || !(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base))
-        return H3_ERR_ARG;
-    if (head_dim != 64 && head_dim != 128) return H3_ERR_SHAPE;
-    if (d_t < 0 || d_h < 0 || d_w < 0 || d_t % 2 || d_h % 2 || d_w % 2 || d_t + d_h + d_w != head_dim)
-        return H3_ERR_SHAPE;
-    // q and k heads fill whole 256-column tiles, and both fit in C's columns
-    const int64_t q_cols = (int64_t)heads * head_dim;
-    if (q_cols % 256 || 2 * q_cols > N) return H3_ERR_SHAPE;
-    if (((uintptr_t)gamma_q & 3) || ((uintptr_t)gamma_k & 3)) return H3_ERR_ALIGN;
     SegTable tab;
-    st = build_segs(segs, n_segs, M, 0, &tab);
-    if (st != H3_OK) return st;
-    if (M == 0) return H3_OK;
     RopeTable rt;
-    fill_rope(head_dim, d_t, d_h, d_w, rope_base, &rt);
+    st = check_qkrope(M, N, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base, segs, n_segs, &tab, &rt);
+    if (st != H3_OK || M == 0) return st;
     return hip_status(launch_gemm_qknorm_rope(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, heads, head_dim,
                                               gamma_q, gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
@@ -420,6 +430,21 @@ h3_status h3_gemm_fp8_swiglu(const void* A, int64_t lda, const float* a_scale, c
     if (M == 0) return H3_OK;
     return hip_status(launch_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K,
                                              (hipStream_t)stream));
+}
+
+h3_status h3_gemm_fp8_qknorm_rope(const void* A, int64_t lda, const float* a_scale, const void* W, int64_t ldw,
+                                  const float* w_scale, void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                                  int32_t heads, int32_t head_dim, const float* gamma_q, const float* gamma_k,
+                                  float eps, int32_t d_t, int32_t d_h, int32_t d_w, float rope_base,
+                                  const h3_segment* segs, int32_t n_segs, void* stream) {
+    h3_status st = check_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, N, 2);
+    if (st != H3_OK) return st;
+    SegTable tab;
+    RopeTable rt;
+    st = check_qkrope(M, N, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base, segs, n_segs, &tab, &rt);
+    if (st != H3_OK || M == 0) return st;
+    return hip_status(launch_gemm_fp8_qknorm_rope(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, heads, head_dim,
+                                                  gamma_q, gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
 
 h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64_t ld, int64_t n_tok, int32_t heads,

@@ -655,10 +655,8 @@ hipError_t launch_gemm_swiglu(bool bf, const void* A, int64_t lda, const void* W
 }
 
 template <int HD>
-static hipError_t launch_qkrope_hd(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
-                                   int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t heads, const float* gq,
-                                   const float* gk, float eps, const RopeTable& rt, const SegTable& tab,
-                                   hipStream_t st) {
+static EpiQkRope<HD> make_qkrope(int32_t heads, const float* gq, const float* gk, float eps, const RopeTable& rt,
+                                 const SegTable& tab) {
     EpiQkRope<HD> e;
     memset(&e, 0, sizeof(e));
     e.gq = gq;
@@ -672,15 +670,27 @@ static hipError_t launch_qkrope_hd(bool bf, const void* A, int64_t lda, const vo
         e.axis[p] = rt.axis[p];
     }
     e.tab = tab;
-    return launch_gemm_epi(bf, A, lda, W, ldw, C, ldc, M, N, K, e, st);
+    return e;
 }
 
 hipError_t launch_gemm_qknorm_rope(bool bf, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                                   int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t heads, int32_t hd,
                                   const float* gq, const float* gk, float eps, const RopeTable& rt,
                                   const SegTable& tab, hipStream_t st) {
-    return hd == 128 ? launch_qkrope_hd<128>(bf, A, lda, W, ldw, C, ldc, M, N, K, heads, gq, gk, eps, rt, tab, st)
-                     : launch_qkrope_hd<64>(bf, A, lda, W, ldw, C, ldc, M, N, K, heads, gq, gk, eps, rt, tab, st);
+    if (hd == 128)
+        return launch_gemm_epi(bf, A, lda, W, ldw, C, ldc, M, N, K, make_qkrope<128>(heads, gq, gk, eps, rt, tab), st);
+    return launch_gemm_epi(bf, A, lda, W, ldw, C, ldc, M, N, K, make_qkrope<64>(heads, gq, gk, eps, rt, tab), st);
+}
+
+hipError_t launch_gemm_fp8_qknorm_rope(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,
+                                      const float* sw, void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                                      int32_t heads, int32_t hd, const float* gq, const float* gk, float eps,
+                                      const RopeTable& rt, const SegTable& tab, hipStream_t st) {
+    if (hd == 128)
+        return launch_gemm_t<fp8, bf16>(A, lda, W, ldw, C, ldc, M, N, K,
+                                        make_qkrope<128>(heads, gq, gk, eps, rt, tab), sa, sw, st);
+    return launch_gemm_t<fp8, bf16>(A, lda, W, ldw, C, ldc, M, N, K, make_qkrope<64>(heads, gq, gk, eps, rt, tab),
+                                    sa, sw, st);
 }
 
 hipError_t launch_gemm_fp8_gate(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,

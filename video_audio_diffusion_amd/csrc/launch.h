@@ -47,6 +47,10 @@ hipError_t launch_gemm_fp8_gate(const void* A, int64_t lda, const float* sa, con
                                 const float* sw, const void* x, void* out, int64_t ldo, int64_t M, int32_t N,
                                 int32_t K, const float* mod, int32_t n_sets, int32_t br, const SegTable& tab,
                                 hipStream_t st);
+hipError_t launch_gemm_fp8_qknorm_rope(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw,
+                                      const float* sw, void* C, int64_t ldc, int64_t M, int32_t N, int32_t K,
+                                      int32_t heads, int32_t hd, const float* gq, const float* gk, float eps,
+                                      const RopeTable& rt, const SegTable& tab, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu(const void* A, int64_t lda, const float* sa, const void* Wgu, int64_t ldw,
                                   const float* sw, void* H, int64_t ldh, int64_t M, int32_t F, int32_t K,
                                   hipStream_t st);
