@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 // buffer of tile j-2.  Odd half steps end with the wavefront's LDS reads
 // complete and all but its last kF8Buf-4 copies landed (tile j+2 at the end
 // of half step 2j+1), then the barrier.
-constexpr int kF8Buf = 6;
+constexpr int kF8Buf = 7;
 
 // Buffer descriptor words of [base, base + bytes), stride 0, as SGPRs (the
 // layout __builtin_amdgcn_make_buffer_rsrc builds; reads past `bytes` give 0).
