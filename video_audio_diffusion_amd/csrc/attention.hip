@@ -373,14 +373,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(
 // in one basic block: a wavefront's own independent VALU instructions are
 // what issue while its MFMAs execute.
 //
-// LDS: K and V tiles of 64 keys (2 blocks) in a ring of three buffers per
-// operand, each operand's three buffers declared together so that every
-// fragment address is a per-lane base plus an immediate offset.  K
-// fragments of block b are read in iteration b-2, V^T fragments in iteration
-// b-1, so tile u is read in iterations 2u-2 .. 2u.  One barrier per tile,
-// before iteration 2u, makes tile u+1 visible (its copies went out one
-// barrier earlier) and frees the buffer of tile u-1, whose reads ended in
-// iteration 2u-2, for the copy of tile u+2.
+// LDS: K and V tiles of 64 keys (2 blocks) in a ring of four buffers per
+// operand (128 KB in all; a workgroup above 128 KB of LDS was measured to
+// run its loop a sixth slower), each operand's buffers declared together so
+// that every fragment address is a per-lane base plus an immediate offset.
+// K fragments of block b are read in iteration b-2, V^T fragments in
+// iteration b-1, so tile u is read in iterations 2u-2 .. 2u.  One barrier per
+// tile, before iteration 2u, makes tile u+1 visible (its copies went out two
+// barriers earlier, tile u+2's one barrier earlier) and frees the buffer of
+// tile u-1, whose reads ended in iteration 2u-2, for the copy of tile u+3.
+// Copies are issued for every tile, past the end too (they read zeros), so
+// each wait can leave exactly one tile's copies outstanding.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int64_t ld,
@@ -397,17 +400,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     static_assert(IPW >= 1 && TILE % (1024 * kAttnWaves) == 0, "tile split");
     static_assert(16 % NCH == 0, "exponentials spread evenly over the QK slots");
 
-    // Three K then three V tile buffers: each operand's ring lies in one
-    // window of less than 64 KB.  Separate objects let the compiler see that
+    // Four K then four V tile buffers: each operand's ring lies in one
+    // window of at most 64 KB.  Separate objects let the compiler see that
     // a copy into one buffer leaves reads of the others free to proceed.
     __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
     __shared__ __attribute__((aligned(1024))) char k_lds2[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds3[TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds2[TILE];
-    auto kbuf = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? k_lds0 : i == 1 ? k_lds1 : k_lds2; };
-    auto vbuf = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? v_lds0 : i == 1 ? v_lds1 : v_lds2; };
+    __shared__ __attribute__((aligned(1024))) char v_lds3[TILE];
+    auto kbuf = [&](int i) __attribute__((always_inline)) -> char* {
+        return i == 0 ? k_lds0 : i == 1 ? k_lds1 : i == 2 ? k_lds2 : k_lds3;
+    };
+    auto vbuf = [&](int i) __attribute__((always_inline)) -> char* {
+        return i == 0 ? v_lds0 : i == 1 ? v_lds1 : i == 2 ? v_lds2 : v_lds3;
+    };
+    constexpr int CPT = 2 * IPW;                 // copies per tile and wavefront
 
     const int G = heads * nqt;
     const int b = blockIdx.x;
@@ -579,39 +589,43 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     using T_ = std::true_type;
     using F_ = std::false_type;
     // Barrier before iteration 2u: this wavefront's copies of tile u+1 have
-    // landed, then everyone's have; tile u-1's buffer takes tile u+2.  No LDS
-    // read needs draining: the last reads of tile u-1 were in iteration 2u-2.
+    // landed (only tile u+2's may be outstanding), then everyone's have;
+    // tile u-1's buffer takes tile u+3.  No LDS read needs draining: the
+    // last reads of tile u-1 were in iteration 2u-2.
     auto tile_barrier = [&](int u, char* free_k, char* free_v) __attribute__((always_inline)) {
-        wait_vm<0, false>();
+        wait_vm<CPT, false>();
         __builtin_amdgcn_s_barrier();
-        if (2 * (u + 2) < NB) copy_tile(free_k, free_v, u + 2);
+        copy_tile(free_k, free_v, u + 3);
     };
-    // Iterations j .. j+5 for j = 6w + 2 (tiles 3w+1 .. 3w+4): ring
+    // Iterations j .. j+7 for j = 8w + 2 (tiles 4w+1 .. 4w+5): ring
     // positions are compile-time constants.
     auto trip = [&](int j, auto chk) __attribute__((always_inline)) {
         const int u = j >> 1;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            if ((i & 1) == 0) tile_barrier(u + i / 2, kbuf((i / 2) % 3), vbuf((i / 2) % 3));
-            step(j + i, chk, kbuf(((4 + i) / 2) % 3), i & 1, vbuf(((3 + i) / 2) % 3), (i + 1) & 1);
+        for (int i = 0; i < 8; ++i) {
+            if ((i & 1) == 0) tile_barrier(u + i / 2, kbuf((i / 2) % 4), vbuf((i / 2) % 4));
+            step(j + i, chk, kbuf(((4 + i) / 2) % 4), i & 1, vbuf(((3 + i) / 2) % 4), (i + 1) & 1);
         }
     };
 
-    // ---- prologue: tiles 0 and 1 visible, tile 2 in flight; block 0's
-    //      logits and V^T, block 1's K
+    // ---- prologue: tiles 0 and 1 visible, tiles 2 and 3 in flight; block
+    //      0's logits and V^T, block 1's K
     zero_lds(k_lds0, TILE, tid);
     zero_lds(k_lds1, TILE, tid);
     zero_lds(k_lds2, TILE, tid);
+    zero_lds(k_lds3, TILE, tid);
     zero_lds(v_lds0, TILE, tid);
     zero_lds(v_lds1, TILE, tid);
     zero_lds(v_lds2, TILE, tid);
+    zero_lds(v_lds3, TILE, tid);
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);
     copy_tile(k_lds0, v_lds0, 0);
     copy_tile(k_lds1, v_lds1, 1);
-    wait_vm<0, false>();
+    copy_tile(k_lds2, v_lds2, 2);
+    copy_tile(k_lds3, v_lds3, 3);
+    wait_vm<2 * CPT, false>();
     __builtin_amdgcn_s_barrier();
-    if (4 < NB) copy_tile(k_lds2, v_lds2, 2);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 0, c);
     s = (f32x16){};
@@ -630,8 +644,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     step(0, T_{}, k_lds1, 0, v_lds0, 1);
     step(1, T_{}, k_lds1, 1, v_lds1, 0);
     int j = 2;
-    for (; j + 6 < NBF; j += 6) trip(j, F_{});   // blocks up to j + 6 complete
-    for (; j < NB; j += 6) trip(j, T_{});
+    for (; j + 8 < NBF; j += 8) trip(j, F_{});   // blocks up to j + 8 complete
+    for (; j < NB; j += 8) trip(j, T_{});
     wait_vm<0, true>();    // no tile copy may land after the workgroup's LDS is released
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
