@@ -710,7 +710,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 // buffer of tile j-2.  Odd half steps end with the wavefront's LDS reads
 // complete and all but its last kF8Buf-4 copies landed (tile j+2 at the end
 // of half step 2j+1), then the barrier.
-constexpr int kF8Buf = 7;
+constexpr int kF8Buf = 8;
 
 // Buffer descriptor words of [base, base + bytes), stride 0, as SGPRs (the
 // layout __builtin_amdgcn_make_buffer_rsrc builds; reads past `bytes` give 0).
@@ -744,7 +744,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
     __shared__ __attribute__((aligned(1024))) char kl[kF8Buf * KT];
     __shared__ __attribute__((aligned(1024))) char vl[kF8Buf * KT];
-    __shared__ int simd_count[4];
+    // The role counters live in the last V^T buffer: they are used only in
+    // the prologue, and that buffer is first written in half step 2, after
+    // the prologue's barrier.  The workgroup then takes exactly 128 KB.
+    int* simd_count = reinterpret_cast<int*>(vl + (kF8Buf - 1) * KT);
 
     const int G = heads * nqt;
     const int b = blockIdx.x;
