@@ -22,4 +22,4 @@ from .block import (  # noqa: F401
 from .stack import shifted_sigma, euler_coefficients, euler_update, stack_forward  # noqa: F401
 from .io import patchify, unpatchify, project_inputs, project_outputs  # noqa: F401
 from .fp8 import (e4m3_decode, e4m3_encode, quantize_rows, gemm_fp8, E4M3_MAX,  # noqa: F401
-                  quantize_qkv, vt_key, vt_layout, dequantize_qkv)
+                  quantize_qkv, dequantize_qkv)

@@ -94,25 +94,6 @@ def quantize_qkv(q, k, v, heads, head_dim):
     return q8, sq, k8, sk, v8, sv
 
 
-def vt_key(p):
-    """Key (within its group of 64) stored at position p of the transposed
-    fp8 v: p = 32 g + b holds key 32 (b // 16) + 8 ((b % 16) // 4) + 4 g + b % 4."""
-    p = np.asarray(p)
-    g, b = p // 32, p % 32
-    return 32 * (b // 16) + 8 * ((b % 16) // 4) + 4 * g + b % 4
-
-
-def vt_layout(v8, heads, head_dim, n_pad):
-    """Codes v8 [n, heads*head_dim] -> [heads, head_dim, n_pad]: transposed,
-    each 64-key group in vt_key order, zero past n."""
-    n = v8.shape[0]
-    full = np.zeros((n_pad, heads, head_dim), np.uint8)
-    full[:n] = v8.reshape(n, heads, head_dim)
-    pos = np.arange(n_pad)
-    src = (pos // 64) * 64 + vt_key(pos % 64)
-    return full[src].transpose(1, 2, 0).copy()
-
-
 def dequantize_qkv(q8, sq, k8, sk, v8, sv, heads, head_dim):
     n = q8.shape[0]
     q = e4m3_decode(q8).reshape(n, heads, head_dim) * np.asarray(sq, np.float64).T[:, :, None]

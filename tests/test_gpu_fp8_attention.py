@@ -25,6 +25,7 @@ import numpy as np
 import pytest
 
 import oracle
+from fp8_layout import vt_key, vt_layout
 from video_audio_diffusion_amd import blk, inputs
 from video_audio_diffusion_amd.block import device_inputs, host_array
 
@@ -81,7 +82,7 @@ def _check_quantiser(h, f, n, H, name):
     for key, want in (("q8", q8), ("k8", k8)):
         bad = np.argwhere(h[key] != want)
         assert bad.size == 0, f"{name}: {key} differs at {bad[:5]}"
-    want_vt = oracle.vt_layout(v8, H, HD, h["n_pad"]).reshape(H * HD, h["n_pad"])
+    want_vt = vt_layout(v8, H, HD, h["n_pad"]).reshape(H * HD, h["n_pad"])
     bad = np.argwhere(h["vt"] != want_vt)
     assert bad.size == 0, f"{name}: vt differs at {bad[:5]}"
     return q8, sq, k8, sk, v8, sv
@@ -258,11 +259,11 @@ def test_768p15s_shape_sampled():
     assert np.array_equal(r["sq"][:, idx].cpu().numpy(), sq)
     assert np.array_equal(r["k8"].index_select(0, idx).cpu().numpy(), k8)
     # V^T: each sampled key sits at its permuted position in its group
-    pos = (rows // 64) * 64 + np.argsort(oracle.vt_key(np.arange(64)))[rows % 64]
+    pos = (rows // 64) * 64 + np.argsort(vt_key(np.arange(64)))[rows % 64]
     vt_cols = r["vt"][:, torch.from_numpy(pos).cuda()].cpu().numpy()        # [H*128, len(rows)]
     assert np.array_equal(vt_cols.T, v8)
     n_pad = r["n_pad"]
-    key_at = (np.arange(n_pad) // 64) * 64 + oracle.vt_key(np.arange(n_pad) % 64)
+    key_at = (np.arange(n_pad) // 64) * 64 + vt_key(np.arange(n_pad) % 64)
     past = torch.from_numpy(np.nonzero(key_at >= n)[0]).cuda()
     assert bool((r["vt"][:, past] == 0).all())                 # positions of keys past the end
     # attention on sampled rows, head by head, from the GPU's own codes
@@ -277,7 +278,7 @@ def test_768p15s_shape_sampled():
         sl = slice(hh * HD, (hh + 1) * HD)
         kd = oracle.e4m3_decode(r["k8"][:, sl].cpu().numpy()) * float(sk_h[hh])
         vt_h = r["vt"][hh * HD:(hh + 1) * HD].cpu().numpy()            # [128, n_pad] permuted keys
-        src = (np.arange(n_pad) // 64) * 64 + oracle.vt_key(np.arange(n_pad) % 64)
+        src = (np.arange(n_pad) // 64) * 64 + vt_key(np.arange(n_pad) % 64)
         vd = np.empty((n, HD))
         ok = src < n
         vd[src[ok]] = oracle.e4m3_decode(vt_h[:, ok].T) * float(sv_h[hh])

@@ -25,6 +25,7 @@ import numpy as np
 import pytest
 
 import oracle
+from fp8_layout import vt_key
 from video_audio_diffusion_amd import blk, inputs
 from video_audio_diffusion_amd.block import (BlockWeights, H3BlockFP8, device_inputs, host_array,
                                              interleave_gate_up)
@@ -210,7 +211,7 @@ def _check_calls(cfg, host, block, r, rows=None, attn_heads=None):
     o = _b16(r["o"], rows)
     heads = range(H) if attn_heads is None else attn_heads
     k8_all, vt_all, q8_rows = r["k8"].cpu().numpy(), r["vt"].cpu().numpy(), _host_rows(r["q8"], rows)
-    src = (np.arange(block.n_pad) // 64) * 64 + oracle.vt_key(np.arange(block.n_pad) % 64)
+    src = (np.arange(block.n_pad) // 64) * 64 + vt_key(np.arange(block.n_pad) % 64)
     ok = src < N
     for hh in heads:
         sl = slice(hh * d, (hh + 1) * d)

@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
+from fp8_layout import vt_key, vt_layout
 
 
 def test_defining_values():
@@ -122,31 +123,52 @@ def test_qkv_quantisation_reduces_to_rows():
 
 
 def test_vt_key_is_a_permutation_and_layout_inverts():
-    keys = oracle.vt_key(np.arange(64))
+    keys = vt_key(np.arange(64))
     assert sorted(keys.tolist()) == list(range(64))
     assert keys[:4].tolist() == [0, 1, 2, 3] and keys[4:8].tolist() == [8, 9, 10, 11]
     assert keys[16:20].tolist() == [32, 33, 34, 35] and keys[32:36].tolist() == [4, 5, 6, 7]
     g = np.random.Generator(np.random.PCG64(22))
     n, H, d, n_pad = 100, 2, 8, 128
     v8 = g.integers(0, 0x7F, size=(n, H * d)).astype(np.uint8)
-    vt = oracle.vt_layout(v8, H, d, n_pad)
+    vt = vt_layout(v8, H, d, n_pad)
     assert vt.shape == (H, d, n_pad)
     for p in (0, 5, 37, 63, 64, 99):
-        key = (p // 64) * 64 + int(oracle.vt_key(p % 64))
+        key = (p // 64) * 64 + int(vt_key(p % 64))
         want = v8[key].reshape(H, d) if key < n else np.zeros((H, d), np.uint8)
         np.testing.assert_array_equal(vt[:, :, p], want)
 
 
 def test_fp8_attention_reference_on_exact_codes():
-    """Operands that e4m3 holds exactly (small integers times power-of-two
-    scales) dequantise to themselves, so the reference is plain attention."""
+    """Operands built to be exact in the quantised form: every slice that
+    shares a scale (a token's head for q, a whole head for k and v) holds
+    +-448 * 2^e once and otherwise e4m3 values times 2^e, so its scale is
+    exactly 2^e and every quotient is an e4m3 value.  The codes then
+    dequantise to exactly the operands, with distinct exponents for q, k and
+    v (so swapped k and v scales would fail), and the reference attention of
+    the dequantised operands is the attention of the operands themselves."""
     g = np.random.Generator(np.random.PCG64(23))
     n, H, d = 40, 2, 8
-    q, k, v = (g.integers(-3, 4, size=(n, H * d)).astype(np.float32) for _ in range(3))
-    q8, sq, k8, sk, v8, sv = oracle.quantize_qkv(q, k, v, H, d)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    exps = {"q": -3, "k": -1, "v": 2}
+    ops = {}
+    for name, e in exps.items():
+        x = oracle.e4m3_decode(g.choice(finite, size=(n, H * d))).astype(np.float64) * 2.0 ** e
+        x = x.reshape(n, H, d)
+        if name == "q":
+            x[np.arange(n), :, g.integers(0, d, size=n)] = 448 * 2.0 ** e     # every (token, head)
+        else:
+            for h in range(H):
+                x[g.integers(0, n), h, g.integers(0, d)] = -448 * 2.0 ** e    # once per head
+        ops[name] = x.reshape(n, H * d).astype(np.float32)
+        assert np.array_equal(ops[name].astype(np.float64), x.reshape(n, H * d))   # fp32 holds them
+    q8, sq, k8, sk, v8, sv = oracle.quantize_qkv(ops["q"], ops["k"], ops["v"], H, d)
+    assert np.all(sq == np.float32(2.0 ** exps["q"]))
+    assert np.all(sk == np.float32(2.0 ** exps["k"])) and np.all(sv == np.float32(2.0 ** exps["v"]))
     qd, kd, vd = oracle.dequantize_qkv(q8, sq, k8, sk, v8, sv, H, d)
-    for a, b in ((qd, q), (kd, k), (vd, v)):
-        np.testing.assert_allclose(a, b, rtol=2 ** -4, atol=1e-12)
+    for got, want in ((qd, ops["q"]), (kd, ops["k"]), (vd, ops["v"])):
+        np.testing.assert_array_equal(got, want.astype(np.float64))
+    ref = oracle.attention(*(ops[k].astype(np.float64) for k in "qkv"), H, d, d ** -0.5)
+    np.testing.assert_array_equal(oracle.attention(qd, kd, vd, H, d, d ** -0.5), ref)
 
 
 def test_fp8_attention_quantisation_error_bound():
@@ -170,7 +192,7 @@ def test_fp8_attention_quantisation_error_bound():
     # a mistake of the kind the GPU layout could make (one 64-key group's
     # values permuted) is far outside that bound
     v_bad = np.array(v)
-    v_bad[:64] = v_bad[oracle.vt_key(np.arange(64))]
+    v_bad[:64] = v_bad[vt_key(np.arange(64))]
     bad = oracle.attention(*dq[:2], oracle.dequantize_qkv(*oracle.quantize_qkv(q, k, v_bad, H, d), H, d)[2],
                            H, d, d ** -0.5)
     assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.15

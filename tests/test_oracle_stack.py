@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
+from torch_block import torch_block
 from video_audio_diffusion_amd import inputs, sampler
 
 
@@ -100,3 +101,57 @@ def test_host_schedule_matches_closed_form():
     np.testing.assert_allclose(tot, [0.0, -1.0, -1.0], atol=1e-12)
     with pytest.raises(ValueError):
         sampler.step_coefficients(segs, 50, 50, dict(inputs.TARGET_SHIFTS))
+
+
+def _stack_blocks(b, n):
+    """n blocks of the tiny stack, each with its own seeded weights and
+    non-zero gates (fp64 copies)."""
+    return [{k: (inputs.widen(v, b.dtype) if k.startswith("w_") else v.astype(np.float64))
+             for k, v in inputs.make_stack_block(b, i).items()} for i in range(n)]
+
+
+def test_stack_is_the_blocks_in_order_then_the_update_of_x():
+    """Three blocks with distinct, non-zero gates: the velocity is the
+    blocks applied one after another to x (assembled independently from
+    torch library routines), and the step moves x -- the stack's input, not
+    the velocity -- by coef * v."""
+    c = inputs.STACK_TINY
+    b = c.block
+    x = inputs.widen(inputs.make_inputs(b, ("x",))["x"], b.dtype)
+    blocks = _stack_blocks(b, 3)
+    for t in blocks:   # both branches of every block contribute
+        assert np.abs(t["mod"][:, 2]).mean() > 0.1 and np.abs(t["mod"][:, 5]).mean() > 0.1
+    assert not np.array_equal(blocks[0]["w_qkv"], blocks[1]["w_qkv"])
+    xn, v = oracle.stack_forward(x, blocks, b, 3, 50, dict(c.shifts))
+    h = x
+    for t in blocks:
+        h = torch_block(dict(t, x=h), b)
+    np.testing.assert_allclose(v, h, rtol=1e-10, atol=1e-10)
+    # the update: hand-evaluated coefficients of step 3 (t 0.94 -> 0.92)
+    t0, t1 = 0.94, 0.92
+    sig = lambda t, s: s * t / (1 + (s - 1) * t)
+    coef = np.zeros(b.n_tok)
+    for s in b.segments:
+        if s.kind in dict(c.shifts):
+            sh = dict(c.shifts)[s.kind]
+            coef[s.start:s.start + s.length] = sig(t1, sh) - sig(t0, sh)
+    assert np.count_nonzero(coef) and np.count_nonzero(coef == 0.0)
+    np.testing.assert_allclose(xn, x + coef[:, None] * h, rtol=1e-10, atol=1e-10)
+    # an update applied to the velocity instead of x would differ
+    assert np.abs((h + coef[:, None] * h) - xn).max() > 1e-2
+
+
+def test_stack_order_matters():
+    """The blocks differ, so running them in another order gives another
+    velocity (a stack that ignored its order, or applied every block to the
+    original x, would not see this)."""
+    c = inputs.STACK_TINY
+    b = c.block
+    x = inputs.widen(inputs.make_inputs(b, ("x",))["x"], b.dtype)
+    blocks = _stack_blocks(b, 3)
+    _, v = oracle.stack_forward(x, blocks, b, 0, 50, dict(c.shifts))
+    _, v_rev = oracle.stack_forward(x, blocks[::-1], b, 0, 50, dict(c.shifts))
+    assert np.abs(v - v_rev).max() > 1e-2
+    # applying every block to the original x and keeping the last is also different
+    last_only = torch_block(dict(blocks[-1], x=x), b)
+    assert np.abs(v - last_only).max() > 1e-2
