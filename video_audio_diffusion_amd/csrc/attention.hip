@@ -709,7 +709,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
 // half step 2j every wavefront issues its share of tile j+kF8Buf-2 into the
 // buffer of tile j-2.  Odd half steps end with the wavefront's LDS reads
 // complete and all but its last kF8Buf-4 copies landed (tile j+2 at the end
-// of half step 2j+1), then the barrier.
+// of half step 2j+1), then the barrier.  That count is exact only because
+// every wave issues the copies of every tile, past the last tile too (those
+// read zeros): with fewer copies in flight the wait would let the tile read
+// next still be on its way.
 constexpr int kF8Buf = 8;
 
 // Buffer descriptor words of [base, base + bytes), stride 0, as SGPRs (the
@@ -800,14 +803,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fp8_kernel(
     const u32x4 vr = rsrc_words(VT + (int64_t)head * 128 * n_pad, (uint32_t)(128 * n_pad));
     const uint32_t kl0 = (uint32_t)(uintptr_t)H3_LDS(kl + wave * 1024);
     const uint32_t vl0 = (uint32_t)(uintptr_t)H3_LDS(vl + wave * 1024);
+    // Tiles past the last one are copied too, through descriptors of zero
+    // bytes (every lane reads 0 and no memory is touched), so that each
+    // wave always has exactly two copies per tile in flight and the fixed
+    // vmcnt of the odd half steps always covers the tile read next.
     auto copy_tile = [&](int t) __attribute__((always_inline)) {
-        if (t >= NT) return;
         const int rem = n - t * 64;
-        const int nvalid = __builtin_amdgcn_readfirstlane(rem < 64 ? rem : 64);
-        const u32x4 kr = rsrc_words(K8 + (int64_t)t * 64 * ldq, (uint32_t)(nvalid * ldq));
+        const int nvalid = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : rem < 64 ? rem : 64);
+        const u32x4 kr = rsrc_words(K8 + (int64_t)(t < NT ? t : 0) * 64 * ldq, (uint32_t)(nvalid * ldq));
+        u32x4 vrt = vr;
+        vrt[2] = t < NT ? vr[2] : 0u;
         const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(t % kF8Buf) * KT);
         lds_dma16(kr, kl0 + slot, kdo, 0u);
-        lds_dma16(vr, vl0 + slot, vdo, (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(t * 64)));
+        lds_dma16(vrt, vl0 + slot, vdo, (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(t < NT ? t * 64 : 0)));
     };
 
     i32x8 kf[2][2];                 // K fragments of the next QK: [key half][d chunk]
