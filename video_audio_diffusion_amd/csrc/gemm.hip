@@ -8,13 +8,16 @@
 //
 // Tile: 256 x 256 per workgroup.  With 8 wavefronts (two per SIMD, so one
 // can issue MFMAs while the other waits) each owns a 128 x 64 panel (4 x 2
-// MFMA blocks); with 4 wavefronts each owns 128 x 128.  Each k-step's A and W
-// tiles (ROWB bytes of K per row) are copied from global memory straight into
-// LDS by buffer->LDS loads into a STAGES-deep ring, so the next steps' copies
-// are in flight while a step is multiplied; the buffer resources stop at row
-// M (N), so tiles that run past the end are padded with zeros.  Fragments
-// are double-buffered in registers per 32-byte k-chunk: the reads of the
-// next chunk are issued before the current chunk's MFMAs.
+// MFMA blocks).  Each k-step's A and W tiles (ROWB bytes of K per row) are
+// staged in a ring of LDS stages; fragments are double-buffered in
+// registers per 32-byte k-chunk: the reads of the next chunk are issued
+// before the current chunk's MFMAs.  Two ways of filling the ring:
+//   * bf16 (gemm_mainloop_staged): global -> registers -> LDS, spread over
+//     the step, each load landing a step before its LDS write;
+//   * fp32 and fp8 (the ring loop in gemm_kernel): buffer -> LDS DMA, one
+//     step's copies issued at the step's barrier.
+// The buffer resources stop at row M (N), so tiles that run past the end are
+// padded with zeros.
 //
 // LDS rows are XOR-swizzled in 16-byte chunks so that the 16 rows of a
 // half-wavefront fragment read fall on 16 distinct 16-byte slots of the
@@ -29,6 +32,31 @@
 #include <type_traits>
 
 namespace h3 {
+
+// Launch configuration.  bf16: the register-staged ring (128 bytes of K per
+// step, two LDS stages, eight wavefronts of 128 x 64), XCD groups 4 tiles
+// high (measured best on the block's four projection shapes).  fp32 and
+// fp8: the LDS-DMA ring with the H3_GEMM_* configuration, groups 2 high.
+// The macros only exist so that other configurations of the same templates
+// can be built and timed.
+#ifndef H3_GEMM_ROWB
+#define H3_GEMM_ROWB 128
+#endif
+#ifndef H3_GEMM_STAGES
+#define H3_GEMM_STAGES 2
+#endif
+#ifndef H3_GEMM_GROUP_M
+#define H3_GEMM_GROUP_M 2
+#endif
+#ifndef H3_GEMM_WAVES
+#define H3_GEMM_WAVES 8
+#endif
+#ifndef H3_GEMM_BF16_STAGED
+#define H3_GEMM_BF16_STAGED 1
+#endif
+#ifndef H3_GEMM_BF16_GROUP_M
+#define H3_GEMM_BF16_GROUP_M 4
+#endif
 
 template <typename T> struct GemmMfma;
 
@@ -175,15 +203,129 @@ struct EpiQkRope {
 template <typename E> struct IsQkRope : std::false_type {};
 template <int HD> struct IsQkRope<EpiQkRope<HD>> : std::true_type {};
 
+// ---------------------------------------------------------------- register-staged ring (bf16)
+// Same tile, wavefront panels, two 64 KB LDS stages, swizzle and fragment
+// layout as the ring loop (256 x 256, 8 wavefronts of 128 x 64, 128 bytes
+// of K per step), but the tiles travel global -> registers -> LDS instead of
+// by LDS DMA, spread over the step: in chunk kk of step s each wavefront
+// writes two of its eight 1 KB pieces of step s+1 (loaded during step s-1)
+// into the stage of step s-1, which every wavefront finished reading before
+// the barrier that opened step s, then loads the same two pieces of step s+2
+// into the same registers.  A load therefore has a whole step to land before
+// its data is written, the loads reach the memory system at an even rate
+// (issuing a step's loads in one burst at the barrier held every
+// wavefront's MFMAs behind them), and the one barrier per step only waits
+// for this wavefront's LDS reads and writes.
+__device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][2], char* ring, const bf16* __restrict__ A,
+                                                     int64_t lda, const bf16* __restrict__ W, int64_t ldw, int32_t M,
+                                                     int32_t N, int32_t K, int m0, int n0, int wave, int lane) {
+    constexpr int ROWB = 128, NWAVES = 8, NJ = 2, KCH = 4;
+    using Geo = GemmGeom<ROWB, 2, NWAVES, 32>;
+    constexpr int TILE = Geo::TILE;                      // 32 KB per operand per stage
+    constexpr int PIECES = Geo::PIECES;                  // 1 KB pieces per wavefront per operand (4)
+    constexpr int NP = 2 * PIECES;                       // pieces per wavefront and step: A 0..3, W 4..7
+    constexpr int PPC = NP / KCH;                        // pieces per chunk (2)
+    static_assert(PIECES == 4 && PPC == 2, "staging layout");
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // piece j of this wavefront: tile rows 32 wave + 8 (j % 4) + lane / 8, its
+    // 16-byte chunk (lane % 8) ^ swizzle, into LDS at the piece's 1 KB + 16 lane
+    const uint32_t ldab = (uint32_t)(lda * 2), ldwb = (uint32_t)(ldw * 2);
+    uint32_t voff[NP];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+        const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
+        const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
+        voff[j] = (uint32_t)row * ldab + c * 16;
+        voff[PIECES + j] = (uint32_t)row * ldwb + c * 16;
+    }
+    const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
+    const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (int64_t)m0 * lda, bytes_a);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * ldw, bytes_w);
+    const int nk = K / 64;
+    u32x4 stg[NP];
+    auto load_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(j < PIECES ? ra : rw, voff[j],
+                                                                                  (uint32_t)ks * ROWB, 0));
+    };
+    auto write_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        char* st = ring + (ks & 1) * 2 * TILE + (j < PIECES ? 0 : TILE) + (wave * PIECES + j % PIECES) * 1024;
+        *reinterpret_cast<u32x4*>(st + lane * 16) = stg[j];
+    };
+
+    const int frow = lane & 31, fhalf = lane >> 5;
+    uint32_t fo[KCH];
+#pragma unroll
+    for (int kk = 0; kk < KCH; ++kk) fo[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, 2 * kk + fhalf) << 4));
+    const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
+    u32x4 fa[2][4], fw[2][NJ];
+    auto read_chunk = [&](int ks, int kk, u32x4 (&a)[4], u32x4 (&w)[NJ]) __attribute__((always_inline)) {
+        const char* st = ring + (ks & 1) * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(st + a_panel + i * 32 * ROWB + fo[kk]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) w[j] = *reinterpret_cast<const u32x4*>(st + w_panel + j * 32 * ROWB + fo[kk]);
+    };
+    // The step barrier as asm with a memory clobber, so that the compiler
+    // keeps every LDS access on its side of it.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: step 0 written to stage 0, step 1 in registers
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) write_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, nk > 1 ? 1 : 0);
+    wait_cnt<63, 0>();
+    barrier();
+    read_chunk(0, 0, fa[0], fw[0]);
+    for (int ks = 0; ks < nk; ++ks) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            // pieces 2 kk, 2 kk + 1: step ks+1 to LDS, then step ks+2 loads.
+            // Past the last step the loads repeat it and the writes go to a
+            // stage nobody reads again: the code stays straight, so the
+            // compiler waits for exactly the load each write needs.
+#pragma unroll
+            for (int q = 0; q < PPC; ++q) write_piece(PPC * kk + q, ks + 1);
+#pragma unroll
+            for (int q = 0; q < PPC; ++q) load_piece(PPC * kk + q, ks + 2 < nk ? ks + 2 : nk - 1);
+            if (kk + 1 < KCH) {
+                read_chunk(ks, kk + 1, fa[(kk + 1) & 1], fw[(kk + 1) & 1]);
+            } else if (ks + 1 < nk) {
+                // this wavefront's reads of step ks and writes of step ks+1
+                // are complete; the barrier makes it so for all of them
+                wait_cnt<63, 0>();
+                barrier();
+                read_chunk(ks + 1, 0, fa[0], fw[0]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) GemmMfma<bf16>::mma(acc[i][j], fa[kk & 1][i], fw[kk & 1][j]);
+        }
+    }
+}
+
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
 // the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
-// quantisation scales) before the epilogue.
-template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, typename EPI>
+// quantisation scales) before the epilogue.  STAGED selects the
+// register-staged ring (bf16); otherwise the LDS-DMA ring loop below runs
+// (fp32 and fp8 operands).
+template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, bool STAGED, typename EPI>
 __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict__ A, int64_t lda,
                                                    const TI* __restrict__ W, int64_t ldw,
                                                    T* __restrict__ C, int64_t ldc, int32_t M, int32_t N,
                                                    int32_t K, int32_t tiles_m, int32_t tiles_n, int32_t group_m,
-                                                   EPI epi, const float* __restrict__ sa,
+                                                   const EPI epi, const float* __restrict__ sa,
                                                    const float* __restrict__ sw) {
     using Op = GemmOp<TI>;
     using Geo = GemmGeom<ROWB, STAGES, NWAVES, Op::CHUNK>;
@@ -215,124 +357,123 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
     const int wm = NWAVES == 4 ? wave >> 1 : wave >> 2;
     const int wn = NWAVES == 4 ? wave & 1 : wave & 3;
 
-    // ---- copy offsets: piece j of this wavefront holds tile rows
-    //      64 wave + ROWS_PER_PIECE j + lane / CPR; LDS slot lane % CPR of the
-    //      row receives the chunk stored there
-    const uint32_t ldab = (uint32_t)(lda * ES), ldwb = (uint32_t)(ldw * ES);
-    uint32_t va[PIECES], vw[PIECES];
-#pragma unroll
-    for (int j = 0; j < PIECES; ++j) {
-        const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
-        const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
-        va[j] = (uint32_t)row * ldab + c * 16;
-        vw[j] = (uint32_t)row * ldwb + c * 16;
-    }
-    const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
-    const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
-    const TI* a_base = A + (int64_t)m0 * lda;
-    const TI* w_base = W + (int64_t)n0 * ldw;
-    auto copy_step = [&](int ks) {
-        char* st = ring + (ks % STAGES) * 2 * TILE;
-        copy_operand<PIECES>(st, wave, a_base, bytes_a, va, (uint32_t)ks * ROWB);
-        copy_operand<PIECES>(st + TILE, wave, w_base, bytes_w, vw, (uint32_t)ks * ROWB);
-    };
-
-    // ---- fragment offsets: row (32 i + frow) of the wave's 128-row panel,
-    //      chunk 2 kk + fhalf; the row's swizzle depends on frow only
-    const int frow = lane & 31, fhalf = lane >> 5;
-    constexpr int CPC = Op::CHUNK / 16;                 // 16-byte slots per k-chunk
-    uint32_t fo[KCH], fo2[KCH];
-#pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) {
-        const int c0 = CPC * kk + fhalf * (CPC / 2);
-        fo[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0) << 4));
-        fo2[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0 + 1) << 4));
-    }
-    const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
-
     f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
-
-    // Fragments are double-buffered per 32-byte k-chunk: chunk kk of a step
-    // lives in register slot kk % 2 (4 A + 4 W 16-byte reads), and the next
-    // chunk's reads are issued before the current chunk's 16 MFMAs.
-    using Frag = typename Op::Frag;
-    Frag fa[2][4], fw[2][NJ];
-    auto read_chunk = [&](int ks, int kk, Frag (&a)[4], Frag (&w)[NJ]) {
-        const char* st = ring + (ks % STAGES) * 2 * TILE;
+    if constexpr (STAGED) {
+        static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2 && NWAVES == 8, "staged shape");
+        gemm_mainloop_staged(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+    } else {
+        // ---- copy offsets: piece j of this wavefront holds tile rows
+        //      64 wave + ROWS_PER_PIECE j + lane / CPR; LDS slot lane % CPR of the
+        //      row receives the chunk stored there
+        const uint32_t ldab = (uint32_t)(lda * ES), ldwb = (uint32_t)(ldw * ES);
+        uint32_t va[PIECES], vw[PIECES];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = Op::read(st + a_panel + i * 32 * ROWB + fo[kk], st + a_panel + i * 32 * ROWB + fo2[kk]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            w[j] = Op::read(st + w_panel + j * 32 * ROWB + fo[kk], st + w_panel + j * 32 * ROWB + fo2[kk]);
-    };
-    auto mfma_chunk = [&](const Frag (&a)[4], const Frag (&w)[NJ]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) Op::mma(acc[i][j], a[i], w[j]);
-    };
-    // Wait until step s has landed in LDS for every wavefront and this
-    // wavefront's reads of the step before are done: at most the copies of
-    // the (up to STAGES - 2) later steps already issued may be outstanding.
-    // Then the stage of step s-1 is free for the copy of step s+STAGES-1.
-    // A plain s_barrier is used: __syncthreads() would also wait for the
-    // later copies.
-    constexpr int PER_STEP = 2 * PIECES;
-    auto step_ready = [&](int s, int nk) {
-        const int later = nk - 1 - s;
-        if constexpr (STAGES >= 4) {
-            if (later >= 2) wait_vm<2 * PER_STEP, true>();
-            else if (later == 1) wait_vm<PER_STEP, true>();
-            else wait_vm<0, true>();
-        } else if constexpr (STAGES == 3) {
-            if (later >= 1) wait_vm<PER_STEP, true>();
-            else wait_vm<0, true>();
-        } else {
-            wait_vm<0, true>();
+        for (int j = 0; j < PIECES; ++j) {
+            const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
+            const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
+            va[j] = (uint32_t)row * ldab + c * 16;
+            vw[j] = (uint32_t)row * ldwb + c * 16;
         }
-        __builtin_amdgcn_s_barrier();
-        if (s + STAGES - 1 < nk) copy_step(s + STAGES - 1);
-    };
-
-    const int nk = K / BK;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) copy_step(s);
-    step_ready(0, nk);
-    read_chunk(0, 0, fa[0], fw[0]);
-    for (int ks = 0; ks < nk; ++ks) {
+        const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
+        const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
+        const TI* a_base = A + (int64_t)m0 * lda;
+        const TI* w_base = W + (int64_t)n0 * ldw;
+        auto copy_step = [&](int ks) {
+            char* st = ring + (ks % STAGES) * 2 * TILE;
+            copy_operand<PIECES>(st, wave, a_base, bytes_a, va, (uint32_t)ks * ROWB);
+            copy_operand<PIECES>(st + TILE, wave, w_base, bytes_w, vw, (uint32_t)ks * ROWB);
+        };
+        // ---- fragment offsets: row (32 i + frow) of the wave's 128-row panel,
+        //      chunk 2 kk + fhalf; the row's swizzle depends on frow only
+        const int frow = lane & 31, fhalf = lane >> 5;
+        constexpr int CPC = Op::CHUNK / 16;                 // 16-byte slots per k-chunk
+        uint32_t fo[KCH], fo2[KCH];
 #pragma unroll
         for (int kk = 0; kk < KCH; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < KCH) {
-                // the previous chunk's reads were issued a chunk of MFMAs ago;
-                // retiring them keeps at most 8 LDS reads in flight (the
-                // counter holds 15)
-                wait_vm<63, true>();
-                read_chunk(ks, kk + 1, fa[(kk + 1) & 1], fw[(kk + 1) & 1]);
-            } else {
-                // This chunk's fragments (read a chunk of MFMAs ago) land
-                // here on every path, so the MFMAs below never wait for the
-                // next step's reads issued after the barrier; without it the
-                // compiler merges the last step's counter state into the
-                // common path and stalls every step on those fresh reads.
-                wait_vm<63, true>();
-                if (ks + 1 < nk) {
-                    step_ready(ks + 1, nk);
-                    read_chunk(ks + 1, 0, fa[0], fw[0]);
+            const int c0 = CPC * kk + fhalf * (CPC / 2);
+            fo[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0) << 4));
+            fo2[kk] = (uint32_t)(frow * ROWB + (Geo::slot(frow, c0 + 1) << 4));
+        }
+        const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
+
+
+        // Fragments are double-buffered per 32-byte k-chunk: chunk kk of a step
+        // lives in register slot kk % 2 (4 A + 4 W 16-byte reads), and the next
+        // chunk's reads are issued before the current chunk's 16 MFMAs.
+        using Frag = typename Op::Frag;
+        Frag fa[2][4], fw[2][NJ];
+        auto read_chunk = [&](int ks, int kk, Frag (&a)[4], Frag (&w)[NJ]) {
+            const char* st = ring + (ks % STAGES) * 2 * TILE;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = Op::read(st + a_panel + i * 32 * ROWB + fo[kk], st + a_panel + i * 32 * ROWB + fo2[kk]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                w[j] = Op::read(st + w_panel + j * 32 * ROWB + fo[kk], st + w_panel + j * 32 * ROWB + fo2[kk]);
+        };
+        auto mfma_chunk = [&](const Frag (&a)[4], const Frag (&w)[NJ]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Op::mma(acc[i][j], a[i], w[j]);
+        };
+        // Wait until step s has landed in LDS for every wavefront and this
+        // wavefront's reads of the step before are done: at most the copies of
+        // the (up to STAGES - 2) later steps already issued may be outstanding.
+        // Then the stage of step s-1 is free for the copy of step s+STAGES-1.
+        // A plain s_barrier is used: __syncthreads() would also wait for the
+        // later copies.
+        constexpr int PER_STEP = 2 * PIECES;
+        auto step_ready = [&](int s, int nk) {
+            const int later = nk - 1 - s;      // copies of min(later, STAGES - 2) later steps may be in flight
+            const int ahead = later < STAGES - 2 ? later : STAGES - 2;
+            if (ahead >= 3) wait_vm<(3 * PER_STEP < 63 ? 3 * PER_STEP : 63), true>();
+            else if (ahead == 2) wait_vm<2 * PER_STEP, true>();
+            else if (ahead == 1) wait_vm<PER_STEP, true>();
+            else wait_vm<0, true>();
+            __builtin_amdgcn_s_barrier();
+            if (s + STAGES - 1 < nk) copy_step(s + STAGES - 1);
+        };
+
+        const int nk = K / BK;
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk) copy_step(s);
+        step_ready(0, nk);
+        read_chunk(0, 0, fa[0], fw[0]);
+        for (int ks = 0; ks < nk; ++ks) {
+#pragma unroll
+            for (int kk = 0; kk < KCH; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 < KCH) {
+                    // the previous chunk's reads were issued a chunk of MFMAs ago;
+                    // retiring them keeps at most 8 LDS reads in flight (the
+                    // counter holds 15)
+                    wait_vm<63, true>();
+                    read_chunk(ks, kk + 1, fa[(kk + 1) & 1], fw[(kk + 1) & 1]);
+                } else {
+                    // This chunk's fragments (read a chunk of MFMAs ago) land
+                    // here on every path, so the MFMAs below never wait for the
+                    // next step's reads issued after the barrier; without it the
+                    // compiler merges the last step's counter state into the
+                    // common path and stalls every step on those fresh reads.
+                    wait_vm<63, true>();
+                    if (ks + 1 < nk) {
+                        step_ready(ks + 1, nk);
+                        read_chunk(ks + 1, 0, fa[0], fw[0]);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);   // the reads above go out before these MFMAs
+                mfma_chunk(fa[kk & 1], fw[kk & 1]);
             }
-            __builtin_amdgcn_sched_barrier(0);   // the reads above go out before these MFMAs
-            mfma_chunk(fa[kk & 1], fw[kk & 1]);
         }
     }
 
-    // ---- epilogue: accumulator (lane, r) -> row 8(r/4) + 4(lane/32) + r%4, col lane%32
+    const int frow = lane & 31, fhalf = lane >> 5;
     const bool full = m0 + kBM <= M && n0 + kBN <= N;
     if constexpr (std::is_same<TI, fp8>::value) {
         // dequantise: acc * sa[row] * sw[col] (rows and columns past M / N
@@ -453,7 +594,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
             constexpr int HD = EPI::kHd;
             constexpr int TB = (int)sizeof(T);
             constexpr int RING = STAGES * 2 * TILE;
-            constexpr int RPASS = RING / (kBN * TB) < kBM ? RING / (kBN * TB) : kBM;
+            constexpr int RAVAIL = RING / (kBN * TB);   // tile rows the ring holds
+            constexpr int RPASS = RAVAIL >= kBM ? kBM : RAVAIL >= 128 ? 128 : RAVAIL >= 64 ? 64 : 32;
             constexpr int CPR = kBN * TB / 16;        // 16-byte chunks per tile row
             constexpr int VN = 16 / TB;               // values per chunk
             constexpr int CPH = HD / VN;              // chunks (lanes) per row of a head
@@ -562,51 +704,38 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
             }
         }
     } else {
-        static_assert(std::is_same<EPI, EpiSwiglu>::value && NJ == 2, "SwiGLU pairs a wavefront's two blocks");
-        // output column of this lane: half the interleaved column index
-        const int hcol = (n0 >> 1) + wn * 32 + frow;
+        static_assert(std::is_same<EPI, EpiSwiglu>::value && NJ % 2 == 0, "SwiGLU pairs a wavefront's blocks");
+        // blocks 2q and 2q+1 of a wavefront are a 32-column gate block and its
+        // up block; their output columns start at half the interleaved index
         const int F = N >> 1;
         auto hval = [&](float gt, float up) __attribute__((always_inline)) {
             return gt / (1.0f + __expf(-gt)) * up;
         };
-        T* hbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + hcol;
-        if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int q = 0; q < NJ / 2; ++q) {
+            const int hcol = ((n0 + wn * NJ * 32) >> 1) + q * 32 + frow;
+            T* hbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + hcol;
+            if (full) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
-                                       hval(acc[i][0][r], acc[i][1][r]));
-        } else {
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                    if (row < M && hcol < F)
+                    for (int r = 0; r < 16; ++r)
                         GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
-                                           hval(acc[i][0][r], acc[i][1][r]));
-                }
+                                           hval(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                        if (row < M && hcol < F)
+                            GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
+                                               hval(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
+                    }
+            }
         }
     }
 }
-
-// Launch configuration (measured best on the block's four projection
-// shapes): 128 bytes of K per step, 2 LDS stages, 8 wavefronts (two per
-// SIMD, 128 x 64 each), XCD groups 2 tiles high.  The macros only exist so
-// that other configurations of the same template can be built and timed.
-#ifndef H3_GEMM_ROWB
-#define H3_GEMM_ROWB 128
-#endif
-#ifndef H3_GEMM_STAGES
-#define H3_GEMM_STAGES 2
-#endif
-#ifndef H3_GEMM_GROUP_M
-#define H3_GEMM_GROUP_M 2
-#endif
-#ifndef H3_GEMM_WAVES
-#define H3_GEMM_WAVES 8
-#endif
 
 template <typename TI, typename TO, typename EPI>
 hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int64_t M,
@@ -614,9 +743,16 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
     const int tiles_m = (int)((M + kBM - 1) / kBM);
     const int tiles_n = (N + kBN - 1) / kBN;
     const int grid = tiles_m * tiles_n;
-    gemm_kernel<TI, TO, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
-        (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, H3_GEMM_GROUP_M, epi,
-        sa, sw);
+    constexpr bool BF = std::is_same<TI, bf16>::value;
+    if constexpr (BF && H3_GEMM_BF16_STAGED) {
+        gemm_kernel<TI, TO, 128, 2, 8, true, EPI><<<grid, 512, 0, st>>>(
+            (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
+            H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+    } else {
+        gemm_kernel<TI, TO, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, false, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
+            (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, H3_GEMM_GROUP_M,
+            epi, sa, sw);
+    }
     return hipGetLastError();
 }
 
