@@ -83,3 +83,4 @@ def oracle_inputs(cfg, host):
 
 def make_device(cfg, host):
     return device_inputs(cfg, host)
+

@@ -96,23 +96,64 @@ def test_c2_deterministic(c2):
         assert torch.equal(r[k], r2[k]), k
 
 
+def peaked_bound(gamma, d_logit_scale=1.0):
+    """Derived tolerance of the bf16 path's attention output and block update
+    against the fp64 oracle when Q/K carry a gain gamma.
+
+    A logit s = scale * sum_d q_d k_d of the bf16 path sees four bf16
+    roundings (unit roundoff u = 2^-9, RMS relative error u / sqrt(3) each):
+    the stored modulated norm a (which q and k are computed from) and the
+    stored q, and likewise for k.  With q and k of RMS gamma per element
+    after the norm, the RMS logit error is
+        ds = sqrt(4) * (u / sqrt(3)) * gamma^2 * sqrt(d) * scale
+           = 2 (u / sqrt(3)) gamma^2            (scale = 1 / sqrt(d)).
+    To first order the attention output moves by sum_j p_j ds_j (v_j - o),
+    i.e. by about ds relative to the spread of v, and the block update
+    inherits that through the output projection.  The tolerance is the
+    arithmetic 2e-2 plus ds for the Frobenius-norm metric and plus 3 ds for
+    the largest element (gamma 1: 0.0223 / 0.0268; gamma 4: 0.056 / 0.128)."""
+    u = 2.0 ** -9
+    ds = 2.0 * (u / np.sqrt(3.0)) * gamma ** 2 * d_logit_scale
+    return TB + ds, TB + 3.0 * ds
+
+
+def assert_within(name, got, ref, tol_f, tol_max, x=None):
+    """Frobenius and max metrics (of out - x beyond output rounding when x is
+    given) against separate bounds."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if x is None:
+        d, base = np.abs(got - ref), ref
+    else:
+        d = np.maximum(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref), 0.0)
+        base = ref - np.asarray(x, np.float64)
+    e_max = d.max() / np.abs(base).max()
+    e_f = np.linalg.norm(d) / np.linalg.norm(base)
+    print(f"  {name}: e_max={e_max:.3e} (tol {tol_max:.3g}) e_F={e_f:.3e} (tol {tol_f:.3g})", flush=True)
+    assert e_max <= tol_max and e_f <= tol_f, name
+
+
 @pytest.mark.parametrize("gamma", [1.0, 4.0])
 def test_small_ragged_block(gamma):
-    """117-token block.  With Q/K gains 4 the logits have std about 16, so
-    the bf16 storage of q and k between calls moves logits by ~0.2 and the
-    end-to-end branch delta inherits that; there the attention kernel is
-    held to the tolerance on its own bf16 inputs and the delta is reported."""
+    """117-token block against the fp64 oracle.  With Q/K gains 4 the logits
+    have std about 16, and the bf16 storage of a, q and k moves them by an
+    RMS 0.036 (peaked_bound): the update and the attention output are held
+    to the derived bound, the output itself to 2e-2, and attention on the
+    path's own stored q, k, v to 2e-2."""
     cfg = _small(gamma)
     host = inputs.make_inputs(cfg)
     dev = make_device(cfg, host)
     r = run_block_steps(cfg, dev)
-    ref = oracle.block_forward(oracle_inputs(cfg, host), cfg)
+    t = oracle_inputs(cfg, host)
+    ref = oracle.block_forward(t, cfg)
     x = inputs.widen(host["x"], "bf16")
     got = widen(r["out"], "bf16")
     assert_close(f"small_out_g{gamma}", got, ref["out"], TB)
     if gamma == 1.0:
         assert_delta_close(f"small_delta_g{gamma}", got, ref["out"], x, TB, "bf16")
         assert_close(f"small_o_g{gamma}", widen(r["o"], "bf16"), ref["o"], TB)
+    tol_f, tol_max = peaked_bound(gamma)
+    assert_within(f"small_delta_g{gamma}_bound", got, ref["out"], tol_f, tol_max, x=x)
+    assert_within(f"small_o_g{gamma}_bound", widen(r["o"], "bf16"), ref["o"], tol_f, tol_max)
     I = cfg.inner
     qkv = widen(r["qkv"], "bf16")
     o_ref = oracle.attention(qkv[:, :I], qkv[:, I:2 * I], qkv[:, 2 * I:], cfg.heads, cfg.head_dim, cfg.scale)

@@ -11,7 +11,8 @@
   block, and at the 15 s 768p workload (92840 tokens, full width, the launch
   configuration the benchmark times) every call on sampled rows against the
   oracle applied to the GPU's own inputs to that call, attention over all
-  keys of every head.
+  keys of every head, and the whole block end to end on sampled rows
+  against the oracle's block from the same input.
 """
 import numpy as np
 import pytest
@@ -152,22 +153,29 @@ def _rows(t, rows):
     return inputs.widen(host_array(t.index_select(0, idx), "bf16"), "bf16")
 
 
-def test_c3_fused_each_call():
+@pytest.fixture(scope="module")
+def c3_run():
     """The benchmark's workload and launch configuration: the fused block at
-    92840 tokens.  Buffers hold the last value of each: qkv (after norm and
-    rotation), o, x1, a (= a2), h and out."""
+    92840 tokens, run once; its buffers hold the last value of each: qkv
+    (after norm and rotation), o, x1, a (= a2), h and out."""
     import torch
-    c = C3
-    I, TB = c.inner, TOL["bf16"]
-    print(f"[c3] drawing inputs for {c.n_tok} tokens", flush=True)
-    host = inputs.make_inputs(c)
-    dev = make_device(c, host)
-    block = _fused_block(c, dev)
+    print(f"[c3] drawing inputs for {C3.n_tok} tokens", flush=True)
+    host = inputs.make_inputs(C3)
+    dev = make_device(C3, host)
+    block = _fused_block(C3, dev)
     print("[c3] running the fused block", flush=True)
     block.forward(dev["x"])
     torch.cuda.synchronize()
+    return host, dev, block, inputs.sample_rows(C3, n_random=160)
+
+
+def test_c3_fused_each_call(c3_run):
+    """Every call of the fused block at 92840 tokens against the oracle
+    applied to the GPU's own inputs to that call."""
+    host, dev, block, rows = c3_run
+    c = C3
+    I, TB = c.inner, TOL["bf16"]
     b = block.buf
-    rows = inputs.sample_rows(c, n_random=160)
     t = oracle_inputs(c, {k: host[k] for k in ("mod", "gamma_q", "gamma_k")})
     mod = t["mod"]
     _, pos = oracle.token_table(c.segments, c.n_tok)
@@ -210,3 +218,21 @@ def test_c3_fused_each_call():
                                rows=rows)
     assert_close("gemm_d_gate", out, ref, TB)
     assert_delta_close("gemm_d_gate delta", out, ref, x1, TB, "bf16")
+
+
+def test_c3_fused_end_to_end(c3_run):
+    """The whole fused block at 92840 tokens against the oracle's block from
+    the same x: the oracle computes K and V for every token (about 1.4e13
+    fp64 flop on the host) and every other step only for the sampled rows
+    (rows are independent given K and V).  out and the block's update
+    out - x within 2e-2 (the update beyond the bf16 rounding of out)."""
+    host, dev, block, rows = c3_run
+    c = C3
+    print(f"[c3] oracle block on {len(rows)} rows (K and V for all {c.n_tok} tokens)", flush=True)
+    ref = oracle.block_forward(oracle_inputs(c, host), c, rows=rows)
+    x = inputs.widen(host["x"][rows], "bf16")
+    b = block.buf
+    assert_close("c3_block_out", _rows(b["out"], rows), ref["out"], TOL["bf16"])
+    assert_delta_close("c3_block_delta", _rows(b["out"], rows), ref["out"], x, TOL["bf16"], "bf16")
+    assert_close("c3_block_x1", _rows(b["x1"], rows), ref["x1"], TOL["bf16"])
+    assert_close("c3_block_o", _rows(b["o"], rows), ref["o"], TOL["bf16"])
