@@ -10,12 +10,15 @@ projections carry the gated residual, the gate/up projection SwiGLU) on one
 stream, inputs already resident in HBM; --unfused times the eleven-call
 form instead.
 
-Prints one JSON line: block tokens/s (`value`), attention TFLOP/s and % of
-the 2.5 PFLOP/s dense bf16 MFMA peak, per-kernel times, the roofline of the
-dominant kernel (attention) and the fp64 oracle timed on host cores on a
-bounded token sample (`cpu_baseline`).
+Prints one JSON line: block tokens/s (`value`, from the median of the timed
+steps' durations), attention TFLOP/s and % of the 2.5 PFLOP/s dense bf16
+MFMA peak, per-kernel times (mean over the timed steps, as a profiler's
+average launch time), the roofline of the dominant kernel (attention) and
+the fp64 oracle timed on host cores on a bounded token sample
+(`cpu_baseline`, with the BLAS library it ran on).
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3] [--unfused]
+    python bench.py --copy-calibration 1024     # known-size copy for counter scaling
 """
 import argparse
 import hashlib
@@ -131,8 +134,12 @@ def cpu_baseline(cfg, host, target_s):
     t0 = time.perf_counter()
     run(perm[32:32 + S])
     el = time.perf_counter() - t0
-    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = sum(p.get("num_threads", 0) for p in pools) or 1
+    vendor = ", ".join(f"{p.get('internal_api', '?')} {p.get('version', '?')}"
+                       + (f" ({p['threading_layer']} threads)" if p.get("threading_layer") else "") for p in pools)
     return {"value": S / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "blas": vendor or "none found", "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{S} random tokens of the {N}-token sequence through all eleven fp64 steps "
                       f"(their own q/k/v included) against a full {N}-key K/V; {el:.1f} s wall"}
 
@@ -548,6 +555,31 @@ def bench_adapters(args):
     print(json.dumps(result), flush=True)
 
 
+def copy_calibration(mib, reps):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel), run
+    `reps` times: the known-size transfer that scales rocprofv3's FETCH_SIZE
+    and WRITE_SIZE counters to bytes.  Prints one JSON line with the bytes
+    moved per launch and the measured copy rate."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        dst.copy_(src)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    med = ms[len(ms) // 2]
+    print(json.dumps({"metric": "device-to-device copy (HBM counter calibration)", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": reps + 1, "median_ms": round(med, 4),
+                      "gbs_read_plus_write": round(2 * n / (med * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -567,6 +599,8 @@ def main():
                     help="time the attention on FP8 operands (quantise + attend) beside the bf16 kernel")
     ap.add_argument("--io", action="store_true",
                     help="time the input/output adapters (patchify, projections, unpatchify) of the workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (scale for the HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -582,6 +616,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
     blk.load()
     if args.io:
         bench_adapters(args)
@@ -654,8 +691,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = ev[0][0][0].elapsed_time(ev[K - 1][-1][0])
-    ms_step = total_ms / K
-    log(f"timed {K} steps: {ms_step:.2f} ms/step (host wall {wall * 1e3 / K:.2f} ms/step)")
+    step_ms = sorted(ev[i][0][0].elapsed_time(ev[i][-1][0]) for i in range(K))
+    ms_step = step_ms[K // 2] if K % 2 else 0.5 * (step_ms[K // 2 - 1] + step_ms[K // 2])
+    log(f"timed {K} steps: median {ms_step:.2f} ms/step, mean {total_ms / K:.2f} "
+        f"(host wall {wall * 1e3 / K:.2f} ms/step)")
 
     # per-kernel time of one pass (summed over the blocks of a stack)
     per = {name: sum(ev[i][b][j].elapsed_time(ev[i][b][j + 1]) for i in range(K) for b in range(n_blk)) / K
@@ -674,7 +713,7 @@ def main():
             k.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = k
     attn_tf = flops["attention"] / (per["attention"] * 1e-3) / 1e12
-    tokens_s = cfg.n_tok * K / (total_ms * 1e-3)
+    tokens_s = cfg.n_tok / (ms_step * 1e-3)
 
     result = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -688,6 +727,8 @@ def main():
                    "rope_split": list(cfg.rope_split), "fused_epilogues": not args.unfused,
                    "global_batch": 1, "seq_len": cfg.n_tok,
                    "parallelism": "none (1 GPU)"},
+        "step_ms": {"median": round(ms_step, 3), "mean": round(total_ms / K, 3), "min": round(step_ms[0], 3),
+                    "max": round(step_ms[-1], 3), "of_steps": K},
         "attention_tflops": round(attn_tf, 1), "attention_pct_peak": round(100 * attn_tf / peak_mm, 2),
         "kernels": kernels,
         "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(attn_tf, 1), "peak": peak_mm,

@@ -151,6 +151,18 @@ h3_status h3_gemm_swiglu(const void* A, int64_t lda, const void* Wgu, int64_t ld
                          void* H, int64_t ldh, int64_t M, int32_t F, int32_t K,
                          h3_dtype dt, void* stream);
 
+/* The row permutation that turns the [gate | up] FFN weight of width F
+ * ([notes] 3.2) into the interleaved Wgu that h3_gemm_swiglu and
+ * h3_gemm_fp8_swiglu read; a copy, done once when weights are loaded:
+ *   w_il row 64u + j = w_gu row 32u + j          (j < 32, gate)
+ *   w_il row 64u + j = w_gu row F + 32u + j - 32 (j >= 32, up)
+ *   w_gu : [2F][K] row stride ld_src (gate rows [0, F), up rows [F, 2F))
+ *   w_il : [2F][K] row stride ld_dst, must not overlap w_gu
+ * F a multiple of 32 (F = 0 is a no-op); K * sizeof(dt) a multiple of 16;
+ * ld_src, ld_dst >= K with rows starting on 16-byte boundaries. */
+h3_status h3_interleave_gate_up(const void* w_gu, int64_t ld_src, void* w_il, int64_t ld_dst,
+                                int32_t F, int32_t K, h3_dtype dt, void* stream);
+
 /* Per-head RMSNorm on Q and K ([notes] 3.2: applied per head, before the
  * positional encoding), then 3-D MM-RoPE ([reading] 5 and 7.4), in place:
  *   u <- gamma * u / sqrt(mean(u^2) + eps)      over each head's head_dim values

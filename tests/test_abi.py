@@ -249,11 +249,29 @@ def test_swiglu_and_gate_validation(lib):
     assert L.h3_gate_residual(x, y, x, 72, 192, P + (2 << 30), 2, 0, segs, 3, 1, 0) == blk.H3_ERR_SEGMENTS
 
 
+def test_interleave_gate_up_validation(lib):
+    L = blk.load()
+    src, dst = P, P + (1 << 32)
+    g = lambda src=src, ls=5376, dst=dst, ld=5376, F=14336, K=5376, dt=0: L.h3_interleave_gate_up(src, ls, dst, ld, F,
+                                                                                                 K, dt, 0)
+    assert g(dt=3) == blk.H3_ERR_DTYPE
+    assert g(src=0) == blk.H3_ERR_ARG
+    assert g(F=-32) == blk.H3_ERR_ARG
+    assert g(F=48) == blk.H3_ERR_SHAPE                        # not a multiple of 32
+    assert g(K=100, ls=100, ld=100) == blk.H3_ERR_SHAPE       # 200-byte rows
+    assert g(ls=5000) == blk.H3_ERR_SHAPE                     # stride below K
+    assert g(ld=5380) == blk.H3_ERR_SHAPE                     # rows off 16-byte boundaries
+    assert g(dst=dst + 8) == blk.H3_ERR_ALIGN
+    assert g(dst=src + 4096) == blk.H3_ERR_ARG                # overlap
+    assert g(F=0) == blk.H3_OK                                # nothing to do
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="needs a machine with no GPU (fake pointers)")
 def test_valid_arguments_without_a_device_report_hip_error(lib):
     assert _adaln() == blk.H3_ERR_HIP
     L = blk.load()
     assert L.h3_swiglu(P, P + (1 << 32), 10, 64, 0, 0) == blk.H3_ERR_HIP
+    assert L.h3_interleave_gate_up(P, 64, P + (1 << 32), 64, 32, 64, 0, 0) == blk.H3_ERR_HIP
 
 
 def test_gemm_gate_residual_validation(lib):

@@ -100,6 +100,27 @@ def test_interleave_rows():
         blk.interleave_gate_up_rows(48)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("F,K,pad_src,pad_dst", [(32, 8, 0, 0), (96, 64, 8, 0), (288, 136, 0, 24), (14336, 64, 0, 8)])
+def test_interleave_gate_up_copy(dtype, F, K, pad_src, pad_dst):
+    """h3_interleave_gate_up moves every row whole to the slot the 32-row
+    interleave names (bit-exact), strided source and destination; the
+    padding columns of the destination stay as they were."""
+    import torch
+    ls, ld = K + pad_src, K + pad_dst
+    w_h = inputs.draw_rows(None, (2 * F, ls), 40 + F, dtype=dtype)
+    w = _dev(w_h)
+    il = torch.full((2 * F, ld), -7.0, dtype=w.dtype, device="cuda")
+    dt = blk.H3_BF16 if dtype == "bf16" else blk.H3_F32
+    blk.h3_interleave_gate_up(w, ls, il, ld, F, K, dt)
+    torch.cuda.synchronize()
+    got = host_array(il, dtype)
+    src = host_array(w, dtype)
+    rows = np.asarray(blk.interleave_gate_up_rows(F))
+    assert np.array_equal(got[:, :K].view(np.uint8), src[rows, :K].view(np.uint8))
+    assert np.all(widen(il, dtype)[:, K:] == -7.0)
+
+
 def _small():
     return inputs.BlockConfig(
         name="ragged-bf16", index=11, dim=256, heads=2, head_dim=128, ffn=512, rope_split=(64, 32, 32),

@@ -24,7 +24,7 @@ EXPORTS = ("h3_status_str", "h3_adaln_modulate", "h3_gemm_bf16", "h3_qknorm_rope
            "h3_attention_fwd", "h3_swiglu", "h3_gate_residual", "h3_euler_update",
            "h3_gemm_gate_residual", "h3_gemm_swiglu", "h3_patchify", "h3_unpatchify", "h3_quantize_fp8",
            "h3_gemm_fp8", "h3_gemm_fp8_gate_residual", "h3_gemm_fp8_swiglu", "h3_quantize_qkv_fp8",
-           "h3_attention_fp8", "h3_gemm_qknorm_rope", "h3_gemm_fp8_qknorm_rope")
+           "h3_attention_fp8", "h3_gemm_qknorm_rope", "h3_gemm_fp8_qknorm_rope", "h3_interleave_gate_up")
 
 
 class H3Segment(ctypes.Structure):
@@ -52,6 +52,7 @@ _SIGS = {
     "h3_gemm_gate_residual": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _P, _I32, _I32,
                               _P],
     "h3_gemm_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P],
+    "h3_interleave_gate_up": [_P, _I64, _P, _I64, _I32, _I32, _I32, _P],
     "h3_gemm_qknorm_rope": [_P, _I64, _P, _I64, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _F, _I32, _I32,
                             _I32, _F, _P, _I32, _I32, _P],
     "h3_patchify": [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P],
@@ -220,6 +221,11 @@ def interleave_gate_up_rows(F: int):
         out.extend(range(32 * u, 32 * u + 32))
         out.extend(range(F + 32 * u, F + 32 * u + 32))
     return out
+
+
+def h3_interleave_gate_up(w_gu, ld_src, w_il, ld_dst, F, K, dt, stream=None):
+    _check("h3_interleave_gate_up", load().h3_interleave_gate_up(ptr(w_gu), ld_src, ptr(w_il), ld_dst, F, K, dt,
+                                                                 _stream(stream)))
 
 
 def h3_qknorm_rope3d(q, k, ld, n_tok, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base,

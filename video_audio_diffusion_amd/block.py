@@ -43,15 +43,19 @@ class BlockWeights:
 
 def interleave_gate_up(weights: BlockWeights, keep_plain: bool = True) -> BlockWeights:
     """Weights with the gate/up rows permuted into the 32-row interleave the
-    fused SwiGLU projection reads (a one-time weight layout step, done with
-    a device gather).  keep_plain=False drops the plain [gate | up] copy."""
+    fused SwiGLU projection reads (a one-time weight layout step,
+    h3_interleave_gate_up on the current stream).  keep_plain=False drops
+    the plain [gate | up] copy."""
     import dataclasses
 
     import torch
-    F = weights.w_gu.shape[0] // 2
-    idx = torch.tensor(blk.interleave_gate_up_rows(F), dtype=torch.int64, device=weights.w_gu.device)
-    il = weights.w_gu.index_select(0, idx).contiguous()
-    return dataclasses.replace(weights, w_gu_il=il, w_gu=weights.w_gu if keep_plain else None)
+    w = weights.w_gu
+    if w.dtype not in (torch.bfloat16, torch.float32) or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w_gu must be a [2F, K] bf16 or fp32 matrix with unit column stride")
+    F, K = w.shape[0] // 2, w.shape[1]
+    il = torch.empty(2 * F, K, dtype=w.dtype, device=w.device)
+    blk.h3_interleave_gate_up(w, w.stride(0), il, K, F, K, blk.H3_BF16 if w.dtype == torch.bfloat16 else blk.H3_F32)
+    return dataclasses.replace(weights, w_gu_il=il, w_gu=w if keep_plain else None)
 
 
 class H3Block:

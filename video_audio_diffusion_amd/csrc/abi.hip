@@ -268,6 +268,21 @@ h3_status h3_swiglu(const void* gu, void* h, int64_t n_tok, int32_t F, h3_dtype 
     return hip_status(launch_swiglu(dt == H3_BF16, gu, h, n_tok, F, (hipStream_t)stream));
 }
 
+h3_status h3_interleave_gate_up(const void* w_gu, int64_t ld_src, void* w_il, int64_t ld_dst, int32_t F,
+                                int32_t K, h3_dtype dt, void* stream) {
+    if (!valid_dt(dt)) return H3_ERR_DTYPE;
+    if (!w_gu || !w_il || F < 0 || K < 1) return H3_ERR_ARG;
+    const int es = esize(dt);
+    if (F % 32 || (K * es) % 16 || (int64_t)F * 2 >= kMaxTok) return H3_ERR_SHAPE;
+    if (ld_src < K || ld_dst < K || (ld_src * es) % 16 || (ld_dst * es) % 16) return H3_ERR_SHAPE;
+    if (!aligned16(w_gu) || !aligned16(w_il)) return H3_ERR_ALIGN;
+    if (overlap(span(w_gu, 2 * (int64_t)F, K, ld_src, es), span(w_il, 2 * (int64_t)F, K, ld_dst, es)))
+        return H3_ERR_ARG;
+    if (F == 0) return H3_OK;
+    return hip_status(launch_interleave_gate_up(w_gu, ld_src * es, w_il, ld_dst * es, F, (int64_t)K * es,
+                                                (hipStream_t)stream));
+}
+
 h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_tok, int32_t dim,
                            const float* mod, int32_t n_sets, h3_branch br, const h3_segment* segs,
                            int32_t n_segs, h3_dtype dt, void* stream) {

@@ -266,6 +266,25 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const T* __restrict__ gu, T
     }
 }
 
+// Gate/up weight rows into the 32-row interleave of the fused SwiGLU GEMM:
+// destination row r of [2F][K] is gate row 32u + j (r = 64u + j, j < 32) or
+// up row 32u + j - 32 (F + ...).  16-byte pieces, grid-stride; rows are
+// K * es bytes with K * es a multiple of 16.
+__global__ __launch_bounds__(256) void interleave_gate_up_kernel(const uint8_t* __restrict__ src, int64_t ld_src,
+                                                               uint8_t* __restrict__ dst, int64_t ld_dst,
+                                                               int32_t F, int64_t row_pieces) {
+    const int64_t total = 2 * (int64_t)F * row_pieces;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = idx / row_pieces;
+        const int64_t c = idx - r * row_pieces;
+        const int64_t j = r & 63;
+        const int64_t s = (r >> 6) * 32 + (j & 31) + (j < 32 ? 0 : F);
+        *reinterpret_cast<u32x4*>(dst + r * ld_dst + c * 16) =
+            *reinterpret_cast<const u32x4*>(src + s * ld_src + c * 16);
+    }
+}
+
 // --------------------------------------------------------------------------
 // Per-head RMSNorm of Q and K, then 3-D MM-RoPE, in place.  One workgroup
 // per token: the token's (cos, sin) per pair are computed once into LDS and
@@ -507,6 +526,14 @@ hipError_t launch_swiglu(bool bf, const void* gu, void* h, int64_t n, int32_t F,
         swiglu_kernel<bf16><<<(unsigned)blocks, 256, 0, st>>>((const bf16*)gu, (bf16*)h, n, F);
     else
         swiglu_kernel<float><<<(unsigned)blocks, 256, 0, st>>>((const float*)gu, (float*)h, n, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_interleave_gate_up(const void* src, int64_t ld_src_bytes, void* dst, int64_t ld_dst_bytes,
+                                     int32_t F, int64_t row_bytes, hipStream_t st) {
+    const int64_t pieces = row_bytes / 16;
+    interleave_gate_up_kernel<<<stream_blocks(2 * (int64_t)F * pieces), 256, 0, st>>>(
+        (const uint8_t*)src, ld_src_bytes, (uint8_t*)dst, ld_dst_bytes, F, pieces);
     return hipGetLastError();
 }
 

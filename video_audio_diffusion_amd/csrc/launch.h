@@ -22,6 +22,8 @@ hipError_t launch_gate_residual(bool bf, const void* x, const void* y, void* out
                                 int32_t dim, const float* mod, int32_t br, const SegTable& tab,
                                 hipStream_t st);
 hipError_t launch_swiglu(bool bf, const void* gu, void* h, int64_t n, int32_t F, hipStream_t st);
+hipError_t launch_interleave_gate_up(const void* src, int64_t ld_src_bytes, void* dst, int64_t ld_dst_bytes,
+                                     int32_t F, int64_t row_bytes, hipStream_t st);
 hipError_t launch_qknorm_rope(bool bf, void* q, void* k, int64_t ld, int32_t n, int32_t heads,
                               int32_t hd, const float* gq, const float* gk, float eps,
                               const RopeTable& rt, const SegTable& tab, hipStream_t st);
