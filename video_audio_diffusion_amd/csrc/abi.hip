@@ -75,6 +75,10 @@ h3_status check_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, con
 }
 
 inline h3_status hip_status(hipError_t e) { return e == hipSuccess ? H3_OK : H3_ERR_HIP; }
+// The launchers report hipGetLastError() after their launches; an error left
+// by an earlier, unrelated HIP call of the thread is cleared first so that
+// it is not taken for this call's.
+inline void clear_last_error() { (void)hipGetLastError(); }
 
 // Per-pair rotation table, exact in double: pair p of a head lies in the
 // t, h or w chunk (widths d_t, d_h, d_w, already checked to sum to
@@ -143,7 +147,7 @@ h3_status h3_adaln_modulate(const void* x, void* y, int64_t n_tok, int32_t dim, 
     const h3_status st = build_segs(segs, n_segs, n_tok, n_sets, &tab);
     if (st != H3_OK) return st;
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_adaln(dt == H3_BF16, x, y, (int32_t)n_tok, dim, mod, (int32_t)br, tab, eps,
+    return clear_last_error(), hip_status(launch_adaln(dt == H3_BF16, x, y, (int32_t)n_tok, dim, mod, (int32_t)br, tab, eps,
                                    (hipStream_t)stream));
 }
 
@@ -152,7 +156,7 @@ h3_status h3_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, v
     const h3_status st = check_gemm(A, lda, W, ldw, C, ldc, M, N, K, N, dt);
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, (hipStream_t)stream));
+    return clear_last_error(), hip_status(launch_gemm(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, (hipStream_t)stream));
 }
 
 h3_status h3_gemm_gate_residual(const void* A, int64_t lda, const void* W, int64_t ldw, const void* x, void* out,
@@ -169,7 +173,7 @@ h3_status h3_gemm_gate_residual(const void* A, int64_t lda, const void* W, int64
     st = build_segs(segs, n_segs, M, n_sets, &tab);
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm_gate(dt == H3_BF16, A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets,
+    return clear_last_error(), hip_status(launch_gemm_gate(dt == H3_BF16, A, lda, W, ldw, x, out, ldo, M, N, K, mod, n_sets,
                                        (int32_t)br, tab, (hipStream_t)stream));
 }
 
@@ -181,7 +185,7 @@ h3_status h3_gemm_swiglu(const void* A, int64_t lda, const void* Wgu, int64_t ld
     const h3_status st = check_gemm(A, lda, Wgu, ldw, H, ldh, M, 2 * F, K, F, dt);
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm_swiglu(dt == H3_BF16, A, lda, Wgu, ldw, H, ldh, M, F, K, (hipStream_t)stream));
+    return clear_last_error(), hip_status(launch_gemm_swiglu(dt == H3_BF16, A, lda, Wgu, ldw, H, ldh, M, F, K, (hipStream_t)stream));
 }
 
 h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok, int32_t heads, int32_t head_dim,
@@ -214,7 +218,7 @@ h3_status h3_qknorm_rope3d(void* q, void* k, int64_t ld, int64_t n_tok, int32_t 
     if (n_tok == 0) return H3_OK;
     RopeTable rt;
     fill_rope(head_dim, d_t, d_h, d_w, rope_base, &rt);
-    return hip_status(launch_qknorm_rope(dt == H3_BF16, q, k, ld, (int32_t)n_tok, heads, head_dim, gamma_q,
+    return clear_last_error(), hip_status(launch_qknorm_rope(dt == H3_BF16, q, k, ld, (int32_t)n_tok, heads, head_dim, gamma_q,
                                          gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
 
@@ -229,7 +233,7 @@ h3_status h3_gemm_qknorm_rope(const void* A, int64_t lda, const void* W, int64_t
     RopeTable rt;
     st = check_qkrope(M, N, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base, segs, n_segs, &tab, &rt);
     if (st != H3_OK || M == 0) return st;
-    return hip_status(launch_gemm_qknorm_rope(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, heads, head_dim,
+    return clear_last_error(), hip_status(launch_gemm_qknorm_rope(dt == H3_BF16, A, lda, W, ldw, C, ldc, M, N, K, heads, head_dim,
                                               gamma_q, gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
 
@@ -253,7 +257,7 @@ h3_status h3_attention_fwd(const void* q, const void* k, const void* v, int64_t 
         return H3_ERR_ARG;
     if (lse && overlap(span(lse, 1, (int64_t)heads * n_tok, 0, 4), so)) return H3_ERR_ARG;
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_attention(dt == H3_BF16, q, k, v, ld_qkv, o, ld_o, (int32_t)n_tok, heads, head_dim,
+    return clear_last_error(), hip_status(launch_attention(dt == H3_BF16, q, k, v, ld_qkv, o, ld_o, (int32_t)n_tok, heads, head_dim,
                                        scale, lse, (hipStream_t)stream));
 }
 
@@ -265,7 +269,7 @@ h3_status h3_swiglu(const void* gu, void* h, int64_t n_tok, int32_t F, h3_dtype 
     const int es = esize(dt);
     if (overlap(span(gu, n_tok, 2 * (int64_t)F, 2 * (int64_t)F, es), span(h, n_tok, F, F, es))) return H3_ERR_ARG;
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_swiglu(dt == H3_BF16, gu, h, n_tok, F, (hipStream_t)stream));
+    return clear_last_error(), hip_status(launch_swiglu(dt == H3_BF16, gu, h, n_tok, F, (hipStream_t)stream));
 }
 
 h3_status h3_interleave_gate_up(const void* w_gu, int64_t ld_src, void* w_il, int64_t ld_dst, int32_t F,
@@ -279,7 +283,7 @@ h3_status h3_interleave_gate_up(const void* w_gu, int64_t ld_src, void* w_il, in
     if (overlap(span(w_gu, 2 * (int64_t)F, K, ld_src, es), span(w_il, 2 * (int64_t)F, K, ld_dst, es)))
         return H3_ERR_ARG;
     if (F == 0) return H3_OK;
-    return hip_status(launch_interleave_gate_up(w_gu, ld_src * es, w_il, ld_dst * es, F, (int64_t)K * es,
+    return clear_last_error(), hip_status(launch_interleave_gate_up(w_gu, ld_src * es, w_il, ld_dst * es, F, (int64_t)K * es,
                                                 (hipStream_t)stream));
 }
 
@@ -298,7 +302,7 @@ h3_status h3_gate_residual(const void* x, const void* y, void* out, int64_t n_to
     const h3_status st = build_segs(segs, n_segs, n_tok, n_sets, &tab);
     if (st != H3_OK) return st;
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_gate_residual(dt == H3_BF16, x, y, out, (int32_t)n_tok, dim, mod, (int32_t)br, tab,
+    return clear_last_error(), hip_status(launch_gate_residual(dt == H3_BF16, x, y, out, (int32_t)n_tok, dim, mod, (int32_t)br, tab,
                                            (hipStream_t)stream));
 }
 
@@ -320,7 +324,7 @@ h3_status h3_euler_update(void* x, const void* v, int64_t n_tok, int32_t dim, co
         c.c[i] = coef[i];
     }
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_euler(dt == H3_BF16, x, v, (int32_t)n_tok, dim, tab, c, (hipStream_t)stream));
+    return clear_last_error(), hip_status(launch_euler(dt == H3_BF16, x, v, (int32_t)n_tok, dim, tab, c, (hipStream_t)stream));
 }
 
 // Shared checks of the patch calls: grid and patch sizes, the vector width,
@@ -349,7 +353,7 @@ h3_status h3_patchify(const void* latent, int32_t T, int32_t H, int32_t W, int32
     const h3_status st = check_patch(latent, tokens, ld, T, H, W, C, pt, ph, pw, dt, &n);
     if (st != H3_OK) return st;
     if (n == 0) return H3_OK;
-    return hip_status(launch_patchify(dt == H3_BF16, latent, tokens, ld, PatchGeom{T, H, W, C, pt, ph, pw}, n,
+    return clear_last_error(), hip_status(launch_patchify(dt == H3_BF16, latent, tokens, ld, PatchGeom{T, H, W, C, pt, ph, pw}, n,
                                       (hipStream_t)stream));
 }
 
@@ -359,7 +363,7 @@ h3_status h3_unpatchify(const void* tokens, int64_t ld, int32_t T, int32_t H, in
     const h3_status st = check_patch(latent, tokens, ld, T, H, W, C, pt, ph, pw, dt, &n);
     if (st != H3_OK) return st;
     if (n == 0) return H3_OK;
-    return hip_status(launch_unpatchify(dt == H3_BF16, tokens, ld, latent, PatchGeom{T, H, W, C, pt, ph, pw},
+    return clear_last_error(), hip_status(launch_unpatchify(dt == H3_BF16, tokens, ld, latent, PatchGeom{T, H, W, C, pt, ph, pw},
                                         (hipStream_t)stream));
 }
 
@@ -375,7 +379,7 @@ h3_status h3_quantize_fp8(const void* x, int64_t ldx, int64_t n_rows, int32_t K,
         overlap(span(scales, 1, n_rows, 0, 4), span(x, n_rows, K, ldx, es)))
         return H3_ERR_ARG;
     if (n_rows == 0) return H3_OK;
-    return hip_status(launch_quantize_fp8(dt == H3_BF16, x, ldx, (int32_t)n_rows, K, q, ldq, scales,
+    return clear_last_error(), hip_status(launch_quantize_fp8(dt == H3_BF16, x, ldx, (int32_t)n_rows, K, q, ldq, scales,
                                           (hipStream_t)stream));
 }
 
@@ -413,7 +417,7 @@ h3_status h3_gemm_fp8(const void* A, int64_t lda, const float* a_scale, const vo
     const h3_status st = check_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, N, esize(out_dt));
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt == H3_BF16,
+    return clear_last_error(), hip_status(launch_gemm_fp8(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, out_dt == H3_BF16,
                                       (hipStream_t)stream));
 }
 
@@ -432,7 +436,7 @@ h3_status h3_gemm_fp8_gate_residual(const void* A, int64_t lda, const float* a_s
     st = build_segs(segs, n_segs, M, n_sets, &tab);
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm_fp8_gate(A, lda, a_scale, W, ldw, w_scale, x, out, ldo, M, N, K, mod, n_sets,
+    return clear_last_error(), hip_status(launch_gemm_fp8_gate(A, lda, a_scale, W, ldw, w_scale, x, out, ldo, M, N, K, mod, n_sets,
                                            (int32_t)br, tab, (hipStream_t)stream));
 }
 
@@ -443,7 +447,7 @@ h3_status h3_gemm_fp8_swiglu(const void* A, int64_t lda, const float* a_scale, c
     const h3_status st = check_gemm_fp8(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, 2 * F, K, F, 2);
     if (st != H3_OK) return st;
     if (M == 0) return H3_OK;
-    return hip_status(launch_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K,
+    return clear_last_error(), hip_status(launch_gemm_fp8_swiglu(A, lda, a_scale, Wgu, ldw, w_scale, H, ldh, M, F, K,
                                              (hipStream_t)stream));
 }
 
@@ -458,7 +462,7 @@ h3_status h3_gemm_fp8_qknorm_rope(const void* A, int64_t lda, const float* a_sca
     RopeTable rt;
     st = check_qkrope(M, N, heads, head_dim, gamma_q, gamma_k, eps, d_t, d_h, d_w, rope_base, segs, n_segs, &tab, &rt);
     if (st != H3_OK || M == 0) return st;
-    return hip_status(launch_gemm_fp8_qknorm_rope(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, heads, head_dim,
+    return clear_last_error(), hip_status(launch_gemm_fp8_qknorm_rope(A, lda, a_scale, W, ldw, w_scale, C, ldc, M, N, K, heads, head_dim,
                                                   gamma_q, gamma_k, eps, rt, tab, (hipStream_t)stream));
 }
 
@@ -487,7 +491,7 @@ h3_status h3_quantize_qkv_fp8(const void* q, const void* k, const void* v, int64
             if (overlap(outs[i], outs[j])) return H3_ERR_ARG;
     }
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_quantize_qkv_fp8(q, k, v, ld, (int32_t)n_tok, heads, q8, k8, vt, n_pad, sq, sk, sv,
+    return clear_last_error(), hip_status(launch_quantize_qkv_fp8(q, k, v, ld, (int32_t)n_tok, heads, q8, k8, vt, n_pad, sq, sk, sv,
                                               (hipStream_t)stream));
 }
 
@@ -513,7 +517,7 @@ h3_status h3_attention_fp8(const void* q8, const void* k8, const void* vt, int64
         overlap(so, span(sv, 1, heads, 0, 4)))
         return H3_ERR_ARG;
     if (n_tok == 0) return H3_OK;
-    return hip_status(launch_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o, ld_o, (int32_t)n_tok, heads, scale,
+    return clear_last_error(), hip_status(launch_attention_fp8(q8, k8, vt, n_pad, sq, sk, sv, o, ld_o, (int32_t)n_tok, heads, scale,
                                            (hipStream_t)stream));
 }
 

@@ -34,11 +34,13 @@
 namespace h3 {
 
 // Launch configuration.  bf16: the register-staged ring (128 bytes of K per
-// step, two LDS stages, eight wavefronts of 128 x 64), XCD groups 4 tiles
-// high (measured best on the block's four projection shapes).  fp32 and
-// fp8: the LDS-DMA ring with the H3_GEMM_* configuration, groups 2 high.
-// The macros only exist so that other configurations of the same templates
-// can be built and timed.
+// step, two LDS stages, eight wavefronts of 128 x 64, one memory instruction
+// issued beside each MFMA), XCD groups 4 tiles high (measured best on the
+// block's four projection shapes; four wavefronts of 128 x 128, one per
+// SIMD, ran the plain products as fast but the gated-residual epilogue
+// slower).  fp32 and fp8: the LDS-DMA ring with the H3_GEMM_* configuration,
+// groups 2 high.  The macros only exist so that other configurations of the
+// same templates can be built and timed.
 #ifndef H3_GEMM_ROWB
 #define H3_GEMM_ROWB 128
 #endif
@@ -53,6 +55,12 @@ namespace h3 {
 #endif
 #ifndef H3_GEMM_BF16_STAGED
 #define H3_GEMM_BF16_STAGED 1
+#endif
+#ifndef H3_GEMM_STAGED_INTERLEAVE
+#define H3_GEMM_STAGED_INTERLEAVE 1
+#endif
+#ifndef H3_GEMM_BF16_WAVES
+#define H3_GEMM_BF16_WAVES 8
 #endif
 #ifndef H3_GEMM_BF16_GROUP_M
 #define H3_GEMM_BF16_GROUP_M 4
@@ -204,29 +212,33 @@ template <typename E> struct IsQkRope : std::false_type {};
 template <int HD> struct IsQkRope<EpiQkRope<HD>> : std::true_type {};
 
 // ---------------------------------------------------------------- register-staged ring (bf16)
-// Same tile, wavefront panels, two 64 KB LDS stages, swizzle and fragment
-// layout as the ring loop (256 x 256, 8 wavefronts of 128 x 64, 128 bytes
-// of K per step), but the tiles travel global -> registers -> LDS instead of
-// by LDS DMA, spread over the step: in chunk kk of step s each wavefront
-// writes two of its eight 1 KB pieces of step s+1 (loaded during step s-1)
+// Same tile, two 64 KB LDS stages, swizzle and fragment layout as the ring
+// loop (256 x 256, 128 bytes of K per step; 8 wavefronts of 128 x 64 or 4 of
+// 128 x 128), but the tiles travel global -> registers -> LDS instead of by
+// LDS DMA, spread over the step: in chunk kk of step s each wavefront
+// writes a quarter of its 1 KB pieces of step s+1 (loaded during step s-1)
 // into the stage of step s-1, which every wavefront finished reading before
-// the barrier that opened step s, then loads the same two pieces of step s+2
+// the barrier that opened step s, then loads the same pieces of step s+2
 // into the same registers.  A load therefore has a whole step to land before
 // its data is written, the loads reach the memory system at an even rate
 // (issuing a step's loads in one burst at the barrier held every
 // wavefront's MFMAs behind them), and the one barrier per step only waits
 // for this wavefront's LDS reads and writes.
-__device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][2], char* ring, const bf16* __restrict__ A,
-                                                     int64_t lda, const bf16* __restrict__ W, int64_t ldw, int32_t M,
-                                                     int32_t N, int32_t K, int m0, int n0, int wave, int lane) {
-    constexpr int ROWB = 128, NWAVES = 8, NJ = 2, KCH = 4;
+template <int NWAVES>
+__device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][NWAVES == 4 ? 4 : 2], char* ring,
+                                                     const bf16* __restrict__ A, int64_t lda,
+                                                     const bf16* __restrict__ W, int64_t ldw, int32_t M, int32_t N,
+                                                     int32_t K, int m0, int n0, int wave, int lane) {
+    constexpr int ROWB = 128, KCH = 4;
     using Geo = GemmGeom<ROWB, 2, NWAVES, 32>;
+    constexpr int NJ = Geo::NJ;
     constexpr int TILE = Geo::TILE;                      // 32 KB per operand per stage
-    constexpr int PIECES = Geo::PIECES;                  // 1 KB pieces per wavefront per operand (4)
-    constexpr int NP = 2 * PIECES;                       // pieces per wavefront and step: A 0..3, W 4..7
-    constexpr int PPC = NP / KCH;                        // pieces per chunk (2)
-    static_assert(PIECES == 4 && PPC == 2, "staging layout");
-    const int wm = wave >> 2, wn = wave & 3;
+    constexpr int PIECES = Geo::PIECES;                  // 1 KB pieces per wavefront per operand (4 or 8)
+    constexpr int NP = 2 * PIECES;                       // pieces per wavefront and step: A first, then W
+    constexpr int PPC = NP / KCH;                        // pieces per chunk (2 or 4)
+    static_assert((NWAVES == 8 && PIECES == 4) || (NWAVES == 4 && PIECES == 8), "staging layout");
+    const int wm = NWAVES == 4 ? wave >> 1 : wave >> 2;
+    const int wn = NWAVES == 4 ? wave & 1 : wave & 3;
 
     // piece j of this wavefront: tile rows 32 wave + 8 (j % 4) + lane / 8, its
     // 16-byte chunk (lane % 8) ^ swizzle, into LDS at the piece's 1 KB + 16 lane
@@ -285,6 +297,79 @@ __device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][2], char* 
     wait_cnt<63, 0>();
     barrier();
     read_chunk(0, 0, fa[0], fw[0]);
+#if H3_GEMM_STAGED_INTERLEAVE
+    // One memory instruction beside each MFMA.  Chunks 0-2 of a step: the
+    // next chunk's fragment reads first, then the piece writes and loads.
+    // Chunk 3: the piece writes, the step barrier, the next step's chunk-0
+    // reads, then the loads.
+    constexpr int NM = 4 * NJ, NR = 4 + NJ;
+    auto mfma_i = [&](int kk, int m) __attribute__((always_inline)) {
+        GemmMfma<bf16>::mma(acc[m / NJ][m % NJ], fa[kk & 1][m / NJ], fw[kk & 1][m % NJ]);
+    };
+    // schedule groups: nops memory instructions of one kind (0 LDS read,
+    // 1 LDS write, 2 global load), each after one of the MFMAs [mi, NM)
+    auto groups = [&](int& mi, int nops, int kind) __attribute__((always_inline)) {
+#pragma unroll
+        for (int o = 0; o < nops; ++o) {
+            if (mi < NM) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                ++mi;
+            }
+            if (kind == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else if (kind == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+    };
+    for (int ks = 0; ks < nk; ++ks) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk) {
+            int mi = 0;
+            if (kk + 1 < KCH) {
+                read_chunk(ks, kk + 1, fa[(kk + 1) & 1], fw[(kk + 1) & 1]);
+#pragma unroll
+                for (int q = 0; q < PPC; ++q) write_piece(PPC * kk + q, ks + 1);
+#pragma unroll
+                for (int q = 0; q < PPC; ++q) load_piece(PPC * kk + q, ks + 2 < nk ? ks + 2 : nk - 1);
+#pragma unroll
+                for (int m = 0; m < NM; ++m) mfma_i(kk, m);
+                groups(mi, NR, 0);
+                groups(mi, PPC, 1);
+                groups(mi, PPC, 2);
+#pragma unroll
+                for (int m = mi; m < NM; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                constexpr int M1 = NM / 4;      // MFMAs before the barrier
+#pragma unroll
+                for (int q = 0; q < PPC; ++q) write_piece(PPC * kk + q, ks + 1);
+#pragma unroll
+                for (int m = 0; m < M1; ++m) mfma_i(kk, m);
+#pragma unroll
+                for (int q = 0; q < PPC; ++q) {
+                    if (q < M1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                }
+#pragma unroll
+                for (int q = PPC; q < M1; ++q) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                // (after the last step the reads fetch a stage nobody uses:
+                // the code stays branch-free, so one schedule covers it)
+                wait_cnt<63, 0>();
+                barrier();
+                read_chunk(ks + 1, 0, fa[0], fw[0]);
+#pragma unroll
+                for (int q = 0; q < PPC; ++q) load_piece(PPC * kk + q, ks + 2 < nk ? ks + 2 : nk - 1);
+#pragma unroll
+                for (int m = M1; m < NM; ++m) mfma_i(kk, m);
+                mi = M1;
+                groups(mi, NR, 0);
+                groups(mi, PPC, 2);
+#pragma unroll
+                for (int m = mi; m < NM; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+#else
     for (int ks = 0; ks < nk; ++ks) {
 #pragma unroll
         for (int kk = 0; kk < KCH; ++kk) {
@@ -313,6 +398,7 @@ __device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][2], char* 
                 for (int j = 0; j < NJ; ++j) GemmMfma<bf16>::mma(acc[i][j], fa[kk & 1][i], fw[kk & 1][j]);
         }
     }
+#endif
 }
 
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
@@ -363,8 +449,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
     if constexpr (STAGED) {
-        static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2 && NWAVES == 8, "staged shape");
-        gemm_mainloop_staged(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+        static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2, "staged shape");
+        gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
     } else {
         // ---- copy offsets: piece j of this wavefront holds tile rows
         //      64 wave + ROWS_PER_PIECE j + lane / CPR; LDS slot lane % CPR of the
@@ -745,7 +831,7 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
     const int grid = tiles_m * tiles_n;
     constexpr bool BF = std::is_same<TI, bf16>::value;
     if constexpr (BF && H3_GEMM_BF16_STAGED) {
-        gemm_kernel<TI, TO, 128, 2, 8, true, EPI><<<grid, 512, 0, st>>>(
+        gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
             (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
             H3_GEMM_BF16_GROUP_M, epi, sa, sw);
     } else {
