@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     constexpr int NCH = RB / 32;                 // QK MFMAs per block
     constexpr int DB = HD / 32;                  // 32-wide d blocks of the output
     constexpr int NPV = 2 * DB;                  // PV MFMAs per block
-    static_assert(IPW >= 1 && TILE % (1024 * kAttnWaves) == 0, "tile split");
+    static_assert(IPW >= 1 && IPW <= 2 && TILE % (1024 * kAttnWaves) == 0, "tile split (two copy slots per step)");
     static_assert(16 % NCH == 0, "exponentials spread evenly over the QK slots");
 
     // Four K then four V tile buffers: each operand's ring lies in one
@@ -487,6 +487,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
         }
         copy_kv_tile2<IPW>(kb, vb, wave, Kp, Vp, hoff, t * BKV, n, BKV, ld, ldb, dk, dv);
     };
+    // One 1 KB piece of tile t (operand op: 0 K, 1 V; piece i of this
+    // wavefront's share) into dst, for copies spread over a step's MFMAs.
+    auto copy_piece = [&](char* dst, int t, int op, int i) __attribute__((always_inline)) {
+        const int p = 64 * (wave * IPW + i) + lane;
+        const int key = p / CH, ph = p % CH;
+        const uint32_t off = (uint32_t)key * ldb + (uint32_t)((ph ^ (op ? vswz<CH>(key) : kswz<CH>(key))) << 4);
+        const int rem = n - t * BKV;
+        const int nvalid = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem < BKV ? rem : BKV));
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc((op ? Vp : Kp) + (int64_t)t * BKV * ld + hoff, (uint32_t)nvalid * ldb);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(dst + (wave * IPW + i) * 1024), 16, off, 0, 0, 0);
+    };
     auto read_k1 = [&](const char* buf, int blk, int c) __attribute__((always_inline)) {
         kf[c] = *reinterpret_cast<const u32x4*>(buf + blk * 32 * RB + ko[c]);
     };
@@ -543,7 +555,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     //
     // kp/b2: buffer and block of block j+2's K (prefetched); vb/b1: those of
     // block j+1's V^T.
-    auto step = [&](int j, auto chk, const char* kp, int b2, const char* vb, int b1) __attribute__((always_inline)) {
+    // cps(c): this step's share of tile copies, issued after QK MFMA c
+    auto step = [&](int j, auto chk, const char* kp, int b2, const char* vb, int b1, auto cps)
+                    __attribute__((always_inline)) {
         constexpr bool CHECK = decltype(chk)::value;   // block j+1 may hold keys past the end
         f32x16 sn = (f32x16){};
         u32x4 pfr[2];
@@ -554,14 +568,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[c]),
                                                          __builtin_bit_cast(bf16x8, qf[c]), sn, 0, 0, 0);
             read_k1(kp, b2, c);
+            cps(c);
         }
         softmax_exp(pfr, rs);
-        // Issue order: each QK MFMA with one K read and its share of the
-        // exponentials (fma, exp, fma, exp, pack, dot2).
+        // Issue order: each QK MFMA with one K read, a tile copy after MFMAs
+        // 1 and 5, and its share of the exponentials (fma, exp, fma, exp,
+        // pack, dot2).
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (c == 1 || c == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 48 / NCH, 0);
         }
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= kRedoSum)) != 0, 0)) {   // rare: raise the reference
@@ -591,20 +608,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     // Barrier before iteration 2u: this wavefront's copies of tile u+1 have
     // landed (only tile u+2's may be outstanding), then everyone's have;
     // tile u-1's buffer takes tile u+3.  No LDS read needs draining: the
-    // last reads of tile u-1 were in iteration 2u-2.
-    auto tile_barrier = [&](int u, char* free_k, char* free_v) __attribute__((always_inline)) {
-        wait_vm<CPT, false>();
-        __builtin_amdgcn_s_barrier();
-        copy_tile(free_k, free_v, u + 3);
-    };
+    // last reads of tile u-1 were in iteration 2u-2.  The copies of tile
+    // u+3 go out a piece at a time inside iterations 2u (K) and 2u+1 (V),
+    // all before the next barrier, so each wait still leaves exactly one
+    // tile's copies in flight (a burst of every wavefront's copies right
+    // after the barrier held their MFMAs back).
+    auto nocp = [](int) __attribute__((always_inline)) {};
     // Iterations j .. j+7 for j = 8w + 2 (tiles 4w+1 .. 4w+5): ring
     // positions are compile-time constants.
     auto trip = [&](int j, auto chk) __attribute__((always_inline)) {
         const int u = j >> 1;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if ((i & 1) == 0) tile_barrier(u + i / 2, kbuf((i / 2) % 4), vbuf((i / 2) % 4));
-            step(j + i, chk, kbuf(((4 + i) / 2) % 4), i & 1, vbuf(((3 + i) / 2) % 4), (i + 1) & 1);
+            const int t = u + i / 2 + 3, op = i & 1;
+            char* dst = op ? vbuf((i / 2) % 4) : kbuf((i / 2) % 4);
+            if (op == 0) {
+                wait_vm<CPT, false>();
+                __builtin_amdgcn_s_barrier();
+            }
+            auto cps = [&](int c) __attribute__((always_inline)) {
+                if (c == 1) copy_piece(dst, t, op, 0);
+                if (c == 5 && IPW > 1) copy_piece(dst, t, op, 1);
+            };
+            step(j + i, chk, kbuf(((4 + i) / 2) % 4), i & 1, vbuf(((3 + i) / 2) % 4), (i + 1) & 1, cps);
         }
     };
 
@@ -641,8 +667,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     m_ref = block_max(s);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) read_k1(k_lds0, 1, c);
-    step(0, T_{}, k_lds1, 0, v_lds0, 1);
-    step(1, T_{}, k_lds1, 1, v_lds1, 0);
+    step(0, T_{}, k_lds1, 0, v_lds0, 1, nocp);
+    step(1, T_{}, k_lds1, 1, v_lds1, 0, nocp);
     int j = 2;
     for (; j + 8 < NBF; j += 8) trip(j, F_{});   // blocks up to j + 8 complete
     for (; j < NB; j += 8) trip(j, T_{});
