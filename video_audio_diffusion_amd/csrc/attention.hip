@@ -34,9 +34,21 @@
 // tile the QK product of the next 32-key block is issued in the same basic
 // block as the softmax of the current one, so the MFMA pipe has independent
 // work while the exponentials run.
+//
+// The layouts above are those of the 32x32x16 kernels (attn_bf16_kernel and
+// the fp32 attn_fwd_kernel).  The bf16 default, attn_bf16_m16_kernel, keeps
+// the work split, tiles, copies and softmax and changes the MFMA shape to
+// 16x16x32; its own layouts are described where it is defined.
 #include "launch.h"
 
 #include <type_traits>
+
+// bf16 kernel: 1 = 16x16x32 MFMAs (attn_bf16_m16_kernel, the default:
+// 1.5-3.8 % faster on the 92840-token sweep), 0 = 32x32x16
+// (attn_bf16_kernel, kept buildable as the reference point).
+#ifndef H3_ATTN_MFMA16
+#define H3_ATTN_MFMA16 1
+#endif
 
 namespace h3 {
 
@@ -693,6 +705,370 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------- bf16 on 16x16x32 MFMAs
+// The same work split, tile ring, copies and barriers as attn_bf16_kernel,
+// on v_mfma_f32_16x16x32_bf16 instead of 32x32x16: the same flops in twice
+// as many MFMAs, which on this part draw less power, so the clock settles
+// about 10 % higher under the same load.  Twice the MFMA issues leave less
+// room beside them for the exponentials, so those are spread evenly: the
+// key-tile-1 half of block j's exponentials runs beside QK of block j+1,
+// the key-tile-0 half of block j+1's beside PV of block j (1.5 VALU
+// instructions per MFMA throughout; with all of a block's exponentials in
+// one phase this kernel was no faster than the 32x32x16 one).
+//
+// Layouts (lane l, c = l % 16, g = l / 16).  A 16x16x32 MFMA takes from
+// lane l row c of A and column c of B over k = 8g .. 8g+7, and leaves rows
+// 4g .. 4g+3 of column c of D in lane l.
+//   QK: S^T = K . Q^T per (16-key tile kt, 16-query tile t, 32-wide d chunk
+//       cc): lane l supplies K[key 16kt + c][d 32cc + 8g ..] from LDS and
+//       Q[query 16t + c][d 32cc + 8g ..] from registers, and holds the
+//       logits of keys 16kt + 4g + i (i < 4) for query 16t + c.
+//   PV: O^T += V^T . P^T per 16-wide d tile and query tile, the 32 keys of
+//       a block as the MFMA's k.  Lane l's B operand is its own 8 weights
+//       of query 16t + c: keys 4g + i (tile 0) then 16 + 4g + i (tile 1),
+//       taken as k = 8g .. 8g+7, so P needs no shuffle.  The A operand
+//       must put V[same keys][d] in the same k slots: the transposing read
+//       (in each 16-lane group lane 4a+e receives value e of lanes a, 4+a,
+//       8+a, 12+a) delivers that when source lane 16g + 4j + a reads the four
+//       d values 4a .. 4a+3 of the tile from key 4g + j (and 16 + 4g + j for
+//       the second half).
+// V rows are stored with their 16-byte chunks XOR-ed by 2 (key mod 8), so
+// the 16 rows x 32 bytes of one transposing read fall two per bank slot.
+template <int CH> __device__ __forceinline__ int vswz16(int key) {
+    return CH >= 16 ? (key & 7) << 1 : ((key >> 1) & 3) << 1;
+}
+
+template <int HD>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_m16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int64_t ld,
+    bf16* __restrict__ O, int64_t ldo, int32_t n, int32_t heads, float sl2, float* __restrict__ lse,
+    int32_t nqt) {
+    constexpr int RB = HD * 2;                   // bytes of one K or V row
+    constexpr int CH = RB / 16;                  // 16-byte chunks per row
+    constexpr int BKV = 64;                      // keys per tile (2 blocks)
+    constexpr int TILE = BKV * RB;               // bytes of one operand tile
+    constexpr int IPW = TILE / (1024 * kAttnWaves);
+    constexpr int NC = HD / 32;                  // 32-wide d chunks (QK)
+    constexpr int DT = HD / 16;                  // 16-wide d tiles (PV, output)
+    constexpr int NG = 2 * NC;                   // QK groups of two MFMAs per block
+    static_assert(IPW >= 1 && IPW <= 2 && TILE % (1024 * kAttnWaves) == 0, "tile split (two copy slots per step)");
+    static_assert(48 % NG == 0, "exponentials spread evenly over the QK groups");
+
+    // V's ring first: its eight per-lane read offsets then reach every V
+    // buffer through the read's 16-bit immediate; K's four take one base.
+    __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds2[TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds3[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds2[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds3[TILE];
+    auto kbuf = [&](int i) __attribute__((always_inline)) -> char* {
+        return i == 0 ? k_lds0 : i == 1 ? k_lds1 : i == 2 ? k_lds2 : k_lds3;
+    };
+    auto vbuf = [&](int i) __attribute__((always_inline)) -> char* {
+        return i == 0 ? v_lds0 : i == 1 ? v_lds1 : i == 2 ? v_lds2 : v_lds3;
+    };
+    constexpr int CPT = 2 * IPW;                 // copies per tile and wavefront
+
+    const int G = heads * nqt;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, local = b >> 3;
+    const int base = G >> 3, extra = G & 7;
+    const int L = xcd * base + (xcd < extra ? xcd : extra) + local;
+    const int head = L / nqt;
+    const int qt = L - head * nqt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, g = lane >> 4;
+    const int q0 = qt * kBQ + wave * 32;
+    const int64_t hoff = (int64_t)head * HD;
+    const uint32_t ldb = (uint32_t)(ld * 2);
+
+    u32x4 qf[2][NC];                             // Q fragments: [query tile][d chunk]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int qi = q0 + 16 * t + c16;
+        const char* src = reinterpret_cast<const char*>(Q + (int64_t)(qi < n ? qi : n - 1) * ld + hoff);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) qf[t][cc] = *reinterpret_cast<const u32x4*>(src + cc * 64 + g * 16);
+    }
+    uint32_t ko[NC];                             // K read: row c16 of a 16-key tile, chunk 4cc + g
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) ko[cc] = (uint32_t)(c16 * RB + (((4 * cc + g) ^ kswz<CH>(c16)) << 4));
+    uint32_t vo[DT];                             // V^T read: key 4g + j, d 16db + 4a
+    {
+        const int j = (lane >> 2) & 3, a = lane & 3;
+        const int kr = 4 * g + j;
+#pragma unroll
+        for (int db = 0; db < DT; ++db)
+            vo[db] = (uint32_t)(kr * RB + (((2 * db + (a >> 1)) ^ vswz16<CH>(kr)) << 4) + (a & 1) * 8);
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) asm volatile("" : "+v"(ko[cc]));
+#pragma unroll
+    for (int db = 0; db < DT; ++db) asm volatile("" : "+v"(vo[db]));
+
+    const int NB = (n + 31) >> 5;    // 32-key blocks
+    const int NBF = n >> 5;          // blocks with 32 valid keys
+
+    f32x4 oacc[DT][2];
+#pragma unroll
+    for (int db = 0; db < DT; ++db) oacc[db][0] = oacc[db][1] = (f32x4){};
+    float m_ref[2], l_run[2] = {0.f, 0.f};
+    f32x4 s[2][2];         // [key tile][query tile] logits of the block whose softmax is next
+    u32x4 kf[2][NC];       // K fragments of the next QK: [key tile][d chunk]
+    u32x4 vf[3];           // V^T fragments of the current PV, three d tiles ahead
+
+    auto mfma16 = [](const u32x4& a, const u32x4& b, f32x4 c) __attribute__((always_inline)) -> f32x4 {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    };
+    // one 1 KB piece (operand op: 0 K, 1 V; piece i of this wavefront) of tile t into dst
+    auto copy_piece = [&](char* dst, int t, int op, int i) __attribute__((always_inline)) {
+        const int p = 64 * (wave * IPW + i) + lane;
+        const int key = p / CH, ph = p % CH;
+        const uint32_t off = (uint32_t)key * ldb + (uint32_t)((ph ^ (op ? vswz16<CH>(key) : kswz<CH>(key))) << 4);
+        const int rem = n - t * BKV;
+        const int nvalid = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem < BKV ? rem : BKV));
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc((op ? Vp : Kp) + (int64_t)t * BKV * ld + hoff, (uint32_t)nvalid * ldb);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(dst + (wave * IPW + i) * 1024), 16, off, 0, 0, 0);
+    };
+    auto read_k = [&](const char* buf, int blk, int kt, int cc) __attribute__((always_inline)) {
+        kf[kt][cc] = *reinterpret_cast<const u32x4*>(buf + blk * 32 * RB + kt * 16 * RB + ko[cc]);
+    };
+    auto read_v = [&](const char* buf, int blk, int db) __attribute__((always_inline)) {
+        const char* vp = buf + blk * 32 * RB + vo[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(H3_LDS_S4(vp + 16 * RB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        vf[db % 3] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
+    };
+    auto mask = [&](f32x4 (&acc)[2][2], int kbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kbase + 16 * kt + 4 * g + i >= n) acc[kt][0][i] = acc[kt][1][i] = -__builtin_inff();
+    };
+    // scaled max of a block for query tile t (the four lanes of a query)
+    auto block_max = [&](int t) __attribute__((always_inline)) -> float {
+        float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][t][0], s[0][t][1]), __builtin_fmaxf(s[0][t][2], s[0][t][3]));
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(s[1][t][0], s[1][t][1]),
+                                                  __builtin_fmaxf(s[1][t][2], s[1][t][3])));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        return mx * sl2;
+    };
+    // exponentials of key tile kt of the logits sv under the current
+    // references, into pfr[t] words 2kt, 2kt+1; rs[t] = their sum
+    auto softmax_half = [&](const f32x4 (&sv)[2][2], int kt, u32x4 (&pfr)[2], float (&rs)[2])
+                            __attribute__((always_inline)) {
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            rs[t] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(sv[kt][t][i], sl2, -m_ref[t]));
+                const float p1 = fast_exp2(__builtin_fmaf(sv[kt][t][i + 1], sl2, -m_ref[t]));
+                const uint32_t w = pack_bf16x2(p0, p1);
+                pfr[t][2 * kt + (i >> 1)] = w;
+                rs[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, rs[t], false);
+            }
+        }
+    };
+    // exponentials of a block under the current references, packed as bf16
+    // pairs in PV's k order; rs[t] = their sum over this lane's 8 keys
+    auto softmax_exp = [&](u32x4 (&pfr)[2], float (&rs)[2]) __attribute__((always_inline)) {
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            rs[t] = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kt][t][i], sl2, -m_ref[t]));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kt][t][i + 1], sl2, -m_ref[t]));
+                    const uint32_t w = pack_bf16x2(p0, p1);
+                    pfr[t][2 * kt + (i >> 1)] = w;
+                    rs[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, rs[t], false);
+                }
+        }
+    };
+
+    // One iteration: QK of block j+1 (with block j+2's K reads and the first
+    // three V^T tiles of block j) beside the key-tile-1 exponentials of
+    // block j; the rare reference raise, decided on block j's whole row sum;
+    // then PV of block j, reading its V^T three d tiles ahead (holding a
+    // whole block of V^T fragments a block ahead, as attn_bf16_kernel does,
+    // does not fit in the registers here), beside the key-tile-0
+    // exponentials of block j+1 -- taken after the raise, so always against
+    // the reference block j+1's other half will use.
+    // kp/b2: buffer and block of block j+2's K; vb/b0: those of block j's V.
+    // Carried between iterations: block j's key-tile-0 weights (words 0, 1
+    // of pfr_a[t]) and their row sums, computed beside the previous PV.
+    u32x4 pfr_a[2];
+    float rs_a[2];
+    auto step = [&](int j, auto chk, const char* kp, int b2, const char* vb, int b0, auto cps)
+                    __attribute__((always_inline)) {
+        constexpr bool CHECK = decltype(chk)::value;
+        f32x4 sn[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sn[kt][0] = sn[kt][1] = (f32x4){};
+        u32x4 pfr[2] = {pfr_a[0], pfr_a[1]};
+        float rs_b[2];
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                sn[kt][0] = mfma16(kf[kt][cc], qf[0][cc], sn[kt][0]);
+                sn[kt][1] = mfma16(kf[kt][cc], qf[1][cc], sn[kt][1]);
+                read_k(kp, b2, kt, cc);
+                cps(2 * cc + kt);
+            }
+#pragma unroll
+        for (int db = 0; db < 3; ++db) read_v(vb, b0, db);
+        softmax_half(s, 1, pfr, rs_b);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (gi < NG - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (gi == 1 || gi == (NG > 5 ? 5 : NG - 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24 / NG, 0);
+        }
+        float rs[2] = {rs_a[0] + rs_b[0], rs_a[1] + rs_b[1]};
+        if (CHECK && __builtin_expect(j + 1 >= NBF, 0)) mask(sn, (j + 1) * 32);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs[0] <= kRedoSum) || !(rs[1] <= kRedoSum)) != 0, 0)) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float m_new = __builtin_fmaxf(m_ref[t], block_max(t));
+                const float alpha = fast_exp2(m_ref[t] - m_new);
+#pragma unroll
+                for (int db = 0; db < DT; ++db) oacc[db][t] *= alpha;
+                l_run[t] *= alpha;
+                m_ref[t] = m_new;
+            }
+            softmax_exp(pfr, rs);
+        }
+        float rs_n[2];
+        softmax_half(sn, 0, pfr_a, rs_n);       // block j+1's key tile 0, beside PV(j)
+#pragma unroll
+        for (int db = 0; db < DT; ++db) {
+            oacc[db][0] = mfma16(vf[db % 3], pfr[0], oacc[db][0]);
+            oacc[db][1] = mfma16(vf[db % 3], pfr[1], oacc[db][1]);
+            if (db + 3 < DT) read_v(vb, b0, db + 3);
+        }
+#pragma unroll
+        for (int db = 0; db < DT; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (db + 3 < DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24 / DT, 0);
+        }
+        l_run[0] += rs[0];
+        l_run[1] += rs[1];
+        rs_a[0] = rs_n[0];
+        rs_a[1] = rs_n[1];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[kt][0] = sn[kt][0], s[kt][1] = sn[kt][1];
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    auto nocp = [](int) __attribute__((always_inline)) {};
+    // Barrier before iteration 2u; the copies of tile u+3 go out a piece at
+    // a time inside iterations 2u (K) and 2u+1 (V).  See attn_bf16_kernel.
+    auto trip = [&](int j, auto chk) __attribute__((always_inline)) {
+        const int u = j >> 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = u + i / 2 + 3, op = i & 1;
+            char* dst = op ? vbuf((i / 2) % 4) : kbuf((i / 2) % 4);
+            if (op == 0) {
+                wait_vm<CPT, false>();
+                __builtin_amdgcn_s_barrier();
+            }
+            auto cps = [&](int gi) __attribute__((always_inline)) {
+                if (gi == 1) copy_piece(dst, t, op, 0);
+                if (gi == (NG > 5 ? 5 : NG - 1) && IPW > 1) copy_piece(dst, t, op, 1);
+            };
+            step(j + i, chk, kbuf(((4 + i) / 2) % 4), i & 1, vbuf(((2 + i) / 2) % 4), i & 1, cps);
+        }
+    };
+
+    // ---- prologue: tiles 0 and 1 visible, tiles 2 and 3 in flight; block
+    //      0's logits and V^T, block 1's K
+    zero_lds(k_lds0, TILE, tid);
+    zero_lds(k_lds1, TILE, tid);
+    zero_lds(k_lds2, TILE, tid);
+    zero_lds(k_lds3, TILE, tid);
+    zero_lds(v_lds0, TILE, tid);
+    zero_lds(v_lds1, TILE, tid);
+    zero_lds(v_lds2, TILE, tid);
+    zero_lds(v_lds3, TILE, tid);
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            copy_piece(kbuf(t), t, 0, i);
+            copy_piece(vbuf(t), t, 1, i);
+        }
+    wait_vm<2 * CPT, false>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) read_k(k_lds0, 0, kt, cc);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = (f32x4){};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt][0] = mfma16(kf[kt][cc], qf[0][cc], s[kt][0]);
+            s[kt][1] = mfma16(kf[kt][cc], qf[1][cc], s[kt][1]);
+        }
+    if (NBF == 0) mask(s, 0);
+    m_ref[0] = block_max(0);
+    m_ref[1] = block_max(1);
+    softmax_half(s, 0, pfr_a, rs_a);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) read_k(k_lds0, 1, kt, cc);
+    step(0, T_{}, k_lds1, 0, v_lds0, 0, nocp);
+    step(1, T_{}, k_lds1, 1, v_lds0, 1, nocp);
+    int j = 2;
+    for (; j + 8 < NBF; j += 8) trip(j, F_{});
+    for (; j < NB; j += 8) trip(j, T_{});
+    wait_vm<0, true>();    // no tile copy may land after the workgroup's LDS is released
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float l_tot = l_run[t] + __shfl_xor(l_run[t], 16, kWave);
+        l_tot += __shfl_xor(l_tot, 32, kWave);
+        const float inv = 1.0f / l_tot;
+        const int qi = q0 + 16 * t + c16;
+        if (qi < n) {
+            bf16* orow = O + (int64_t)qi * ldo + hoff + 4 * g;
+#pragma unroll
+            for (int db = 0; db < DT; ++db) {
+                const f32x4& a = oacc[db][t];
+                *reinterpret_cast<u32x2*>(orow + 16 * db) =
+                    (u32x2){pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
+            }
+            if (lse && g == 0) lse[(int64_t)head * n + qi] = m_ref[t] * 0.69314718055994531f + __logf(l_tot);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- fp8 attention
 // head_dim 128, operands from the fp8 quantisation of q, k and v: Q8 and K8
 // [n][heads * 128] e4m3 codes, VT [heads][128][n_pad] (v transposed, each
@@ -1041,12 +1417,21 @@ hipError_t launch_attention(bool bf, const void* q, const void* k, const void* v
     attn_fwd_kernel<TY, D><<<grid, kAttnThreads, 0, st>>>((const TY*)q, (const TY*)k, (const TY*)v, ld,  \
                                                           (TY*)o, ldo, n, heads, sl2, lse, nqt)
     if (bf) {
+#if H3_ATTN_MFMA16
+        if (hd == 128)
+            attn_bf16_m16_kernel<128><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
+                                                                      ld, (bf16*)o, ldo, n, heads, sl2, lse, nqt);
+        else
+            attn_bf16_m16_kernel<64><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
+                                                                     ld, (bf16*)o, ldo, n, heads, sl2, lse, nqt);
+#else
         if (hd == 128)
             attn_bf16_kernel<128><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                                                   (bf16*)o, ldo, n, heads, sl2, lse, nqt);
         else
             attn_bf16_kernel<64><<<grid, kAttnThreads, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                                                  (bf16*)o, ldo, n, heads, sl2, lse, nqt);
+#endif
     } else {
         if (hd == 128) H3_ATTN(float, 128);
         else H3_ATTN(float, 64);
