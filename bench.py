@@ -42,11 +42,15 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources and of the build script that sets their
+    compiler flags (either changes the code the counters were taken on)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "video_audio_diffusion_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files.append(os.path.join(ROOT, "video_audio_diffusion_amd", "build.py"))
+    for path in files:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
