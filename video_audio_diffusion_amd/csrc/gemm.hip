@@ -65,6 +65,9 @@ namespace h3 {
 #ifndef H3_GEMM_BF16_GROUP_M
 #define H3_GEMM_BF16_GROUP_M 4
 #endif
+#ifndef H3_GEMM_MFMA16
+#define H3_GEMM_MFMA16 1
+#endif
 
 template <typename T> struct GemmMfma;
 
@@ -401,11 +404,204 @@ __device__ __forceinline__ void gemm_mainloop_staged(f32x16 (&acc)[4][NWAVES == 
 #endif
 }
 
+// ---------------------------------------------------------------- staged ring on 16x16x32 MFMAs (bf16)
+// The same ring, pieces and barrier as gemm_mainloop_staged, with
+// v_mfma_f32_16x16x32_bf16 (the same flops in twice as many MFMAs, which
+// draw less power, so the part holds a higher clock).  Lane l supplies row
+// (l % 16) of a 16-row block and the 16 bytes at (l / 16) * 16 of a 64-byte
+// k-chunk, so a 128-byte step row holds two chunks.  A wavefront's 128-row
+// A panel is 8 blocks and its W panel 2 NJ blocks; 16x16 block (ib, jb) is
+// sub-block 2 (ib % 2) + (jb % 2) of the 32x32 block (ib / 2, jb / 2) of acc,
+// four floats each (column l % 16, rows 4 (l / 16) .. + 3 of the sub-block).
+//
+// Each chunk is eight regions, one per A block ib: its 2 NJ MFMAs with
+// memory instructions slotted between them.  A fragments rotate through one
+// set of registers: A block ib of the next chunk is read in region ib + 1,
+// after the last MFMA that uses the current one (block 7 in region 0 of the
+// chunk that uses it); W fragments are double-buffered.  Chunk 0: W reads
+// and piece writes in regions 0-3, loads in regions 4-7.  Chunk 1: the
+// writes in regions 0-1, then the step barrier, then the next step's W
+// reads and the loads in regions 2-5.
+template <int NWAVES>
+__device__ __forceinline__ void gemm_mainloop_staged16(f32x16 (&acc)[4][NWAVES == 4 ? 4 : 2], char* ring,
+                                                       const bf16* __restrict__ A, int64_t lda,
+                                                       const bf16* __restrict__ W, int64_t ldw, int32_t M, int32_t N,
+                                                       int32_t K, int m0, int n0, int wave, int lane) {
+    constexpr int ROWB = 128, KCH = 2;
+    using Geo = GemmGeom<ROWB, 2, NWAVES, 64>;
+    constexpr int NJ = Geo::NJ;
+    constexpr int NB = 2 * NJ;                           // 16-column W blocks per wavefront
+    constexpr int TILE = Geo::TILE;
+    constexpr int PIECES = Geo::PIECES;
+    constexpr int NP = 2 * PIECES;                       // pieces per wavefront and step: A first, then W
+    constexpr int PPC = NP / KCH;                        // pieces per chunk (4 or 8)
+    static_assert((NWAVES == 8 && PIECES == 4) || (NWAVES == 4 && PIECES == 8), "staging layout");
+    static_assert(NB % 4 == 0 && PPC % 4 == 0, "region split");
+    const int wm = NWAVES == 4 ? wave >> 1 : wave >> 2;
+    const int wn = NWAVES == 4 ? wave & 1 : wave & 3;
+
+    const uint32_t ldab = (uint32_t)(lda * 2), ldwb = (uint32_t)(ldw * 2);
+    uint32_t voff[NP];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+        const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
+        const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
+        voff[j] = (uint32_t)row * ldab + c * 16;
+        voff[PIECES + j] = (uint32_t)row * ldwb + c * 16;
+    }
+    const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
+    const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (int64_t)m0 * lda, bytes_a);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * ldw, bytes_w);
+    const int nk = K / 64;
+    u32x4 stg[NP];
+    auto load_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(j < PIECES ? ra : rw, voff[j],
+                                                                                  (uint32_t)ks * ROWB, 0));
+    };
+    auto write_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        char* st = ring + (ks & 1) * 2 * TILE + (j < PIECES ? 0 : TILE) + (wave * PIECES + j % PIECES) * 1024;
+        *reinterpret_cast<u32x4*>(st + lane * 16) = stg[j];
+    };
+
+    // fragment offset of chunk kc inside a 16-row block: the block's first
+    // row is even and a multiple of 16, so the swizzle only depends on l % 16
+    const int frow = lane & 15, fq = lane >> 4;
+    uint32_t fo[KCH];
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) fo[kc] = (uint32_t)(frow * ROWB + (Geo::slot(frow, 4 * kc + fq) << 4));
+    const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
+    u32x4 fa[8], fw[2][NB];
+    auto read_a = [&](int ks, int kc, int ib) __attribute__((always_inline)) {
+        fa[ib] = *reinterpret_cast<const u32x4*>(ring + (ks & 1) * 2 * TILE + a_panel + ib * 16 * ROWB + fo[kc]);
+    };
+    auto read_w = [&](int ks, int kc, int jb) __attribute__((always_inline)) {
+        fw[kc][jb] = *reinterpret_cast<const u32x4*>(ring + (ks & 1) * 2 * TILE + w_panel + jb * 16 * ROWB + fo[kc]);
+    };
+    auto mfma = [&](int kc, int ib, int jb) __attribute__((always_inline)) {
+        f32x16& c = acc[ib >> 1][jb >> 1];
+        const int b = 4 * (2 * (ib & 1) + (jb & 1));
+        f32x4 d = {c[b], c[b + 1], c[b + 2], c[b + 3]};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[ib]),
+                                                    __builtin_bit_cast(bf16x8, fw[kc][jb]), d, 0, 0, 0);
+        c[b] = d[0];
+        c[b + 1] = d[1];
+        c[b + 2] = d[2];
+        c[b + 3] = d[3];
+    };
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the issue order of a region: one memory instruction after each MFMA,
+    // LDS reads first, then LDS writes, then global loads
+    auto order = [&](int nrd, int nwr, int nld) __attribute__((always_inline)) {
+        int m = 0;
+#pragma unroll
+        for (int o = 0; o < nrd + nwr + nld; ++o) {
+            if (m < NB) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                ++m;
+            }
+            if (o < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else if (o < nrd + nwr) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (; m < NB; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: step 0 written to stage 0, step 1 in registers, the
+    //      fragments of step 0's chunk 0 except A block 7
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) write_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, nk > 1 ? 1 : 0);
+    wait_cnt<63, 0>();
+    barrier();
+#pragma unroll
+    for (int ib = 0; ib < 7; ++ib) read_a(0, 0, ib);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) read_w(0, 0, jb);
+    __builtin_amdgcn_sched_barrier(0);
+
+    constexpr int W4 = NB / 4, P4 = PPC / 4, P2 = PPC / 2;
+    for (int ks = 0; ks < nk; ++ks) {
+        const int kn = ks + 2 < nk ? ks + 2 : nk - 1;    // loads past the last step repeat it
+        // ---- chunk 0
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            if (ib == 0) read_a(ks, 0, 7);
+            else read_a(ks, 1, ib - 1);
+            if (ib < 4) {
+#pragma unroll
+                for (int q = 0; q < W4; ++q) read_w(ks, 1, W4 * ib + q);
+#pragma unroll
+                for (int q = 0; q < P4; ++q) write_piece(P4 * ib + q, ks + 1);
+            } else {
+#pragma unroll
+                for (int q = 0; q < P4; ++q) load_piece(P4 * (ib - 4) + q, kn);
+            }
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) mfma(0, ib, jb);
+            if (ib < 4) order(1 + W4, P4, 0);
+            else order(1, 0, P4);
+        }
+        // ---- chunk 1
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            if (ib < 2) {
+                if (ib == 0) read_a(ks, 1, 7);
+#pragma unroll
+                for (int q = 0; q < P2; ++q) write_piece(PPC + P2 * ib + q, ks + 1);
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) mfma(1, ib, jb);
+                order(ib == 0 ? 1 : 0, P2, 0);
+                if (ib == 1) {
+                    // this wavefront's reads of step ks and writes of step
+                    // ks+1 are done; the barrier makes it so for all of them
+                    // (after the last step the reads below fetch a stage
+                    // nobody uses: the code stays branch-free)
+                    wait_cnt<63, 0>();
+                    barrier();
+                }
+            } else {
+                if (ib == 2) read_a(ks + 1, 0, 0);
+                read_a(ks + 1, 0, ib - 1);
+                if (ib < 6) {
+#pragma unroll
+                    for (int q = 0; q < W4; ++q) read_w(ks + 1, 0, W4 * (ib - 2) + q);
+#pragma unroll
+                    for (int q = 0; q < P4; ++q) load_piece(PPC + P4 * (ib - 2) + q, kn);
+                }
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) mfma(1, ib, jb);
+                order((ib == 2 ? 2 : 1) + (ib < 6 ? W4 : 0), 0, ib < 6 ? P4 : 0);
+            }
+        }
+    }
+}
+
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
 // the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
 // quantisation scales) before the epilogue.  STAGED selects the
 // register-staged ring (bf16); otherwise the LDS-DMA ring loop below runs
 // (fp32 and fp8 operands).
+// row and column of accumulator element r inside its 32x32 block, less the
+// lane's own offsets (lrow, lcol in gemm_kernel)
+template <bool M16>
+__device__ __forceinline__ constexpr int acc_row(int r) {
+    return M16 ? 16 * (r >> 3) + (r & 3) : 8 * (r >> 2) + (r & 3);
+}
+template <bool M16>
+__device__ __forceinline__ constexpr int acc_col(int r) {
+    return M16 ? 16 * ((r >> 2) & 1) : 0;
+}
+
 template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, bool STAGED, typename EPI>
 __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict__ A, int64_t lda,
                                                    const TI* __restrict__ W, int64_t ldw,
@@ -443,6 +639,15 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
     const int wm = NWAVES == 4 ? wave >> 1 : wave >> 2;
     const int wn = NWAVES == 4 ? wave & 1 : wave & 3;
 
+    // Accumulator layout.  Element r of 32x32 block (i, j) is output row
+    // 32 i + erow(r) + lrow and column 32 j + ecol(r) + lcol of the
+    // wavefront's panel: for the 32x32 MFMA rows 8 (r / 4) + r % 4 + 4 (l / 32)
+    // of column l % 32; for 16x16x32 sub-block r / 4 holds rows
+    // 16 (r / 8) + r % 4 + 4 (l / 16 % 4) of column 16 (r / 4 % 2) + l % 16.
+    constexpr bool M16 = STAGED && H3_GEMM_MFMA16;
+    const int lrow = M16 ? 4 * ((lane >> 4) & 3) : 4 * (lane >> 5);
+    const int lcol = M16 ? lane & 15 : lane & 31;
+
     f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -450,7 +655,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
     if constexpr (STAGED) {
         static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2, "staged shape");
-        gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+        if constexpr (M16) gemm_mainloop_staged16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+        else gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
     } else {
         // ---- copy offsets: piece j of this wavefront holds tile rows
         //      64 wave + ROWS_PER_PIECE j + lane / CPR; LDS slot lane % CPR of the
@@ -559,30 +765,35 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         }
     }
 
-    const int frow = lane & 31, fhalf = lane >> 5;
     const bool full = m0 + kBM <= M && n0 + kBN <= N;
+    // CB column halves per 32x32 block take their own column-indexed values
+    constexpr int CB = M16 ? 2 : 1;
+    auto rof = [](int r) __attribute__((always_inline)) { return acc_row<M16>(r); };
+    auto cof = [](int r) __attribute__((always_inline)) { return acc_col<M16>(r); };
     if constexpr (std::is_same<TI, fp8>::value) {
         // dequantise: acc * sa[row] * sw[col] (rows and columns past M / N
         // take scale 0 and are never stored)
-        float cs[NJ];
+        float cs[NJ][CB];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int col = n0 + wn * NJ * 32 + j * 32 + frow;
-            cs[j] = col < N ? sw[col] : 0.f;
-        }
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int h = 0; h < CB; ++h) {
+                const int col = n0 + wn * NJ * 32 + j * 32 + 16 * h + lcol;
+                cs[j][h] = col < N ? sw[col] : 0.f;
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                const int row = m0 + wm * 128 + i * 32 + rof(r) + lrow;
                 const float rs = row < M ? sa[row] : 0.f;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[i][j][r] *= rs * cs[j];
+                for (int j = 0; j < NJ; ++j) acc[i][j][r] *= rs * cs[j][cof(r) >> 4];
             }
     }
     // plain store of the accumulators (rows and columns past M, N skipped)
     auto store_c = [&]() __attribute__((always_inline)) {
-        T* cbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
+        T* cbase = C + (int64_t)(m0 + wm * 128 + lrow) * ldc + n0 + wn * NJ * 32 + lcol;
         if (full) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -590,19 +801,18 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                 for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
-                                           acc[i][j][r]);
+                        GemmMfma<T>::store(cbase + (int64_t)(i * 32 + rof(r)) * ldc + j * 32 + cof(r), acc[i][j][r]);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int col = n0 + wn * NJ * 32 + j * 32 + frow;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                        const int row = m0 + wm * 128 + i * 32 + rof(r) + lrow;
+                        const int col = n0 + wn * NJ * 32 + j * 32 + cof(r) + lcol;
                         if (row < M && col < N)
-                            GemmMfma<T>::store(cbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
+                            GemmMfma<T>::store(cbase + (int64_t)(i * 32 + rof(r)) * ldc + j * 32 + cof(r),
                                                acc[i][j][r]);
                     }
                 }
@@ -620,16 +830,20 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         const int set0 = epi.tab.s[seg0].mod_set;
         // gates of this lane's columns: loaded once for a one-set tile, per row
         // (from cache) on the few tiles an interval boundary crosses
-        const float* gbase = epi.mod + (int64_t)epi.chunk * N + n0 + wn * NJ * 32 + frow;
+        const float* gbase = epi.mod + (int64_t)epi.chunk * N + n0 + wn * NJ * 32 + lcol;
         const int64_t set_stride = (int64_t)6 * N;
-        float g0[NJ];
+        float g0[NJ][CB];
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-            g0[j] = n0 + wn * NJ * 32 + j * 32 + frow < N ? gbase[set0 * set_stride + j * 32] : 0.f;
-        auto gate = [&](int row, int j) __attribute__((always_inline)) {
-            return one_set ? g0[j] : gbase[epi.tab.s[find_seg(epi.tab, row)].mod_set * set_stride + j * 32];
+#pragma unroll
+            for (int h = 0; h < CB; ++h)
+                g0[j][h] = n0 + wn * NJ * 32 + j * 32 + 16 * h + lcol < N
+                               ? gbase[set0 * set_stride + j * 32 + 16 * h] : 0.f;
+        auto gate = [&](int row, int j, int r) __attribute__((always_inline)) {
+            return one_set ? g0[j][cof(r) >> 4]
+                           : gbase[epi.tab.s[find_seg(epi.tab, row)].mod_set * set_stride + j * 32 + cof(r)];
         };
-        const int64_t obase = (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + n0 + wn * NJ * 32 + frow;
+        const int64_t obase = (int64_t)(m0 + wm * 128 + lrow) * ldc + n0 + wn * NJ * 32 + lcol;
         if (full) {
             // per 32-row block: all 16 x NJ residual loads first, then the stores
 #pragma unroll
@@ -639,15 +853,14 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                 for (int r = 0; r < 16; ++r)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        xv[r][j] = GemmMfma<T>::load(xb + obase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc +
-                                                     j * 32);
+                        xv[r][j] = GemmMfma<T>::load(xb + obase + (int64_t)(i * 32 + rof(r)) * ldc + j * 32 + cof(r));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    const int row = m0 + wm * 128 + i * 32 + rof(r) + lrow;
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        GemmMfma<T>::store(C + obase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32,
-                                           xv[r][j] + gate(row, j) * acc[i][j][r]);
+                        GemmMfma<T>::store(C + obase + (int64_t)(i * 32 + rof(r)) * ldc + j * 32 + cof(r),
+                                           xv[r][j] + gate(row, j, r) * acc[i][j][r]);
                 }
             }
         } else {
@@ -655,14 +868,14 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    const int row = m0 + wm * 128 + i * 32 + rof(r) + lrow;
                     if (row >= M) continue;
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) {
-                        const int col = n0 + wn * NJ * 32 + j * 32 + frow;
+                        const int col = n0 + wn * NJ * 32 + j * 32 + cof(r) + lcol;
                         if (col >= N) continue;
                         const int64_t o = (int64_t)row * ldc + col;
-                        GemmMfma<T>::store(C + o, GemmMfma<T>::load(xb + o) + gate(row, j) * acc[i][j][r]);
+                        GemmMfma<T>::store(C + o, GemmMfma<T>::load(xb + o) + gate(row, j, r) * acc[i][j][r]);
                     }
                 }
         }
@@ -733,10 +946,10 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                     if ((wm * 128 + i * 32) / RPASS != pass) continue;
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) {
-                        const int col = wn * NJ * 32 + j * 32 + frow;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int rl = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3) - pass * RPASS;
+                            const int col = wn * NJ * 32 + j * 32 + cof(r) + lcol;
+                            const int rl = wm * 128 + i * 32 + rof(r) + lrow - pass * RPASS;
                             reinterpret_cast<T*>(chunk_at(rl, col / VN))[col % VN] = (T)acc[i][j][r];
                         }
                     }
@@ -799,23 +1012,23 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         };
 #pragma unroll
         for (int q = 0; q < NJ / 2; ++q) {
-            const int hcol = ((n0 + wn * NJ * 32) >> 1) + q * 32 + frow;
-            T* hbase = C + (int64_t)(m0 + wm * 128 + 4 * fhalf) * ldc + hcol;
+            const int hcol = ((n0 + wn * NJ * 32) >> 1) + q * 32 + lcol;
+            T* hbase = C + (int64_t)(m0 + wm * 128 + lrow) * ldc + hcol;
             if (full) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
+                        GemmMfma<T>::store(hbase + (int64_t)(i * 32 + rof(r)) * ldc + cof(r),
                                            hval(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                        if (row < M && hcol < F)
-                            GemmMfma<T>::store(hbase + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc,
+                        const int row = m0 + wm * 128 + i * 32 + rof(r) + lrow;
+                        if (row < M && hcol + cof(r) < F)
+                            GemmMfma<T>::store(hbase + (int64_t)(i * 32 + rof(r)) * ldc + cof(r),
                                                hval(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
                     }
             }
