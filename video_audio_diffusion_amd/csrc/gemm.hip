@@ -478,16 +478,19 @@ __device__ __forceinline__ void gemm_mainloop_staged16(f32x16 (&acc)[4][NWAVES =
     auto read_w = [&](int ks, int kc, int jb) __attribute__((always_inline)) {
         fw[kc][jb] = *reinterpret_cast<const u32x4*>(ring + (ks & 1) * 2 * TILE + w_panel + jb * 16 * ROWB + fo[kc]);
     };
+    // the loop accumulates into plain 4-register tuples (slices of acc's
+    // 16-register vectors made the compiler copy them between AGPRs and
+    // VGPRs around every MFMA once they no longer fit in the VGPRs); they
+    // are packed into acc after the loop
+    f32x4 c16[8][NB];
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) c16[ib][jb] = (f32x4){};
     auto mfma = [&](int kc, int ib, int jb) __attribute__((always_inline)) {
-        f32x16& c = acc[ib >> 1][jb >> 1];
-        const int b = 4 * (2 * (ib & 1) + (jb & 1));
-        f32x4 d = {c[b], c[b + 1], c[b + 2], c[b + 3]};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[ib]),
-                                                    __builtin_bit_cast(bf16x8, fw[kc][jb]), d, 0, 0, 0);
-        c[b] = d[0];
-        c[b + 1] = d[1];
-        c[b + 2] = d[2];
-        c[b + 3] = d[3];
+        c16[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[ib]),
+                                                              __builtin_bit_cast(bf16x8, fw[kc][jb]), c16[ib][jb],
+                                                              0, 0, 0);
     };
     auto barrier = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
@@ -584,6 +587,12 @@ __device__ __forceinline__ void gemm_mainloop_staged16(f32x16 (&acc)[4][NWAVES =
             }
         }
     }
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[ib >> 1][jb >> 1][4 * (2 * (ib & 1) + (jb & 1)) + e] = c16[ib][jb][e];
 }
 
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
