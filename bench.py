@@ -41,16 +41,46 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text, hash_comments):
+    """text without its comments (C and C++ comments, or '#' comments for
+    Python), string and character literals kept as written."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif not hash_comments and text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif not hash_comments and text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif hash_comments and c == "#":
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
+
+
 def kernel_source_hash():
     """Hash of the kernel sources and of the build script that sets their
-    compiler flags (either changes the code the counters were taken on)."""
+    compiler flags (either changes the code the counters were taken on).
+    Comments and blank lines are left out, so an edit of the documentation
+    alone keeps the counters valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "video_audio_diffusion_amd", "csrc")
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
     files.append(os.path.join(ROOT, "video_audio_diffusion_amd", "build.py"))
     for path in files:
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + fh.read())
+        with open(path, encoding="utf-8") as fh:
+            code = _code_only(fh.read(), hash_comments=path.endswith(".py"))
+        h.update(os.path.basename(path).encode() + code.encode())
     return h.hexdigest()[:16]
 
 

@@ -1,19 +1,21 @@
 // C = A . W^T on MFMA for the four projections of the H3 block.
 //
 // A [M][K] and W [N][K] are both K-contiguous, which is exactly the operand
-// layout of the 32x32 MFMA: lane l supplies row (l % 32) and a 16-byte run of
-// k at offset (l / 32) * 16 bytes inside a 32-byte k-chunk.  So both operands
-// are staged in LDS as [rows][128 bytes of k] tiles and read back as whole
-// 16-byte vectors.
+// layout of the MFMAs: for 32x32 lane l supplies row (l % 32) and a 16-byte
+// run of k at offset (l / 32) * 16 bytes inside a 32-byte k-chunk; for
+// 16x16x32 (the bf16 default) row (l % 16) and the 16 bytes at (l / 16) * 16
+// of a 64-byte chunk.  So both operands are staged in LDS as [rows][128 bytes
+// of k] tiles and read back as whole 16-byte vectors.
 //
 // Tile: 256 x 256 per workgroup.  With 8 wavefronts (two per SIMD, so one
 // can issue MFMAs while the other waits) each owns a 128 x 64 panel (4 x 2
-// MFMA blocks).  Each k-step's A and W tiles (ROWB bytes of K per row) are
+// blocks of 32x32, or 8 x 4 of 16x16).  Each k-step's A and W tiles (ROWB bytes of K per row) are
 // staged in a ring of LDS stages; fragments are double-buffered in
 // registers per 32-byte k-chunk: the reads of the next chunk are issued
 // before the current chunk's MFMAs.  Two ways of filling the ring:
-//   * bf16 (gemm_mainloop_staged): global -> registers -> LDS, spread over
-//     the step, each load landing a step before its LDS write;
+//   * bf16 (gemm_mainloop_staged16 on 16x16x32 MFMAs, the default, or
+//     gemm_mainloop_staged on 32x32x16): global -> registers -> LDS, spread
+//     over the step, each load landing a step before its LDS write;
 //   * fp32 and fp8 (the ring loop in gemm_kernel): buffer -> LDS DMA, one
 //     step's copies issued at the step's barrier.
 // The buffer resources stop at row M (N), so tiles that run past the end are
@@ -35,10 +37,9 @@ namespace h3 {
 
 // Launch configuration.  bf16: the register-staged ring (128 bytes of K per
 // step, two LDS stages, eight wavefronts of 128 x 64, one memory instruction
-// issued beside each MFMA), XCD groups 4 tiles high (measured best on the
-// block's four projection shapes; four wavefronts of 128 x 128, one per
-// SIMD, ran the plain products as fast but the gated-residual epilogue
-// slower).  fp32 and fp8: the LDS-DMA ring with the H3_GEMM_* configuration,
+// issued beside each MFMA) on 16x16x32 MFMAs, XCD groups 4 tiles high
+// (measured best on the block's four projection shapes; four wavefronts of
+// 128 x 128, one per SIMD, ran about 4 % slower).  fp32 and fp8: the LDS-DMA ring with the H3_GEMM_* configuration,
 // groups 2 high.  The macros only exist so that other configurations of the
 // same templates can be built and timed.
 #ifndef H3_GEMM_ROWB
