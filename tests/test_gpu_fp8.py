@@ -61,6 +61,33 @@ def test_quantize_bit_exact(dtype, n, K, pad):
         assert np.all(got_q[:, K:] == 0x55), "wrote past K"
 
 
+@pytest.mark.parametrize("K", [4096, 7168, 11264, 14336, 20480])
+def test_quantize_bit_exact_widths(K):
+    """Every row width class of the bf16 quantiser (rows held in registers up
+    to 14336 values, the general kernel beyond), and rows holding an
+    infinity, which take the general arithmetic: a scale of inf, codes 0
+    (0x80 for negative values) and 0x7F for the infinity itself (inf / inf).
+    Rows holding a NaN are left out: the oracle's NaN-propagating max and the
+    kernel's max differ there, and nothing specifies that case."""
+    n = 7
+    x = inputs.draw_rows(None, (n, K), 950 + K, dtype="bf16")
+    x[1] = 0
+    x[2, 7] = inputs.store(np.array([2.5e4], np.float32), "bf16")[0]
+    x[3, K // 3] = inputs.store(np.array([np.inf], np.float32), "bf16")[0]
+    x[4, K - 1] = inputs.store(np.array([-np.inf], np.float32), "bf16")[0]
+    x[5, 5:9] = inputs.store(np.array([1e-4, -2e-4, 3e-6, -0.0], np.float32), "bf16")
+    w = inputs.widen(x, "bf16").astype(np.float32)
+    q, s = _quantize(_dev(x), n, K, "bf16")
+    import torch
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        q_ref, s_ref = oracle.quantize_rows(w)
+    got_s = s.cpu().numpy()
+    assert np.array_equal(got_s, s_ref), f"scales differ: {got_s} {s_ref}"
+    got_q = q.cpu().numpy()
+    assert np.array_equal(got_q, q_ref), f"codes differ at {np.argwhere(got_q != q_ref)[:5]}"
+
+
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (255, 200, 384), (513, 1032, 1024), (300, 264, 5376)])
 def test_gemm_fp8_against_oracle(out, M, N, K):
