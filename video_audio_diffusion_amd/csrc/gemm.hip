@@ -69,6 +69,9 @@ namespace h3 {
 #ifndef H3_GEMM_MFMA16
 #define H3_GEMM_MFMA16 1
 #endif
+#ifndef H3_GEMM_FP8_STAGED
+#define H3_GEMM_FP8_STAGED 1
+#endif
 
 template <typename T> struct GemmMfma;
 
@@ -596,6 +599,171 @@ __device__ __forceinline__ void gemm_mainloop_staged16(f32x16 (&acc)[4][NWAVES =
             for (int e = 0; e < 4; ++e) acc[ib >> 1][jb >> 1][4 * (2 * (ib & 1) + (jb & 1)) + e] = c16[ib][jb][e];
 }
 
+// ---------------------------------------------------------------- staged ring for fp8 operands
+// The register-staged ring of gemm_mainloop_staged16 (same pieces, loads a
+// step ahead, LDS writes, barrier) for e4m3 operands on the 32x32x64 MFMA of
+// the ring loop (lane l supplies row l % 32 and the 32 bytes at (l / 32) * 32
+// of a 64-byte k-chunk: two 16-byte slots), so the accumulators keep the
+// 32x32 layout and the products equal the ring loop's.  A 128-byte step row
+// holds two chunks; a chunk is four regions, one per 32-row A block, each
+// its two MFMAs (64 cycles each) with the memory instructions after them.
+// A fragments rotate through one set of registers (block i of the next
+// chunk is read in region i + 1, block 3 in region 0 of the chunk that uses
+// it); W fragments are double-buffered.
+__device__ __forceinline__ void gemm_mainloop_staged_fp8(f32x16 (&acc)[4][2], char* ring,
+                                                         const uint8_t* __restrict__ A, int64_t lda,
+                                                         const uint8_t* __restrict__ W, int64_t ldw, int32_t M,
+                                                         int32_t N, int32_t K, int m0, int n0, int wave, int lane) {
+    constexpr int NWAVES = 8, ROWB = 128, KCH = 2;
+    using Geo = GemmGeom<ROWB, 2, NWAVES, 64>;
+    constexpr int TILE = Geo::TILE;
+    constexpr int PIECES = Geo::PIECES;                  // 4
+    constexpr int NP = 2 * PIECES;
+    constexpr int PPC = NP / KCH;                        // 4 pieces per chunk
+    static_assert(PIECES == 4 && Geo::NJ == 2, "staging layout");
+    using Op = GemmOp<fp8>;
+    using Frag = Op::Frag;
+    const int wm = wave >> 2, wn = wave & 3;
+
+    const uint32_t ldab = (uint32_t)lda, ldwb = (uint32_t)ldw;
+    uint32_t voff[NP];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+        const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
+        const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
+        voff[j] = (uint32_t)row * ldab + c * 16;
+        voff[PIECES + j] = (uint32_t)row * ldwb + c * 16;
+    }
+    const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
+    const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (int64_t)m0 * lda, bytes_a);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * ldw, bytes_w);
+    const int nk = K / ROWB;
+    u32x4 stg[NP];
+    auto load_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(j < PIECES ? ra : rw, voff[j],
+                                                                                  (uint32_t)ks * ROWB, 0));
+    };
+    auto write_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        char* st = ring + (ks & 1) * 2 * TILE + (j < PIECES ? 0 : TILE) + (wave * PIECES + j % PIECES) * 1024;
+        *reinterpret_cast<u32x4*>(st + lane * 16) = stg[j];
+    };
+
+    // fragment slots of chunk kc: 4 kc + 2 (l / 32) and the next, in row l % 32
+    // of a 32-row block (block starts are multiples of 32: the swizzle only
+    // depends on l % 32)
+    const int frow = lane & 31, fhalf = lane >> 5;
+    uint32_t fo[KCH][2];
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            fo[kc][h] = (uint32_t)(frow * ROWB + (Geo::slot(frow, 4 * kc + 2 * fhalf + h) << 4));
+    const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * 2 * 32 * ROWB;
+    Frag fa[4], fw[2][2];
+    auto read_a = [&](int ks, int kc, int i) __attribute__((always_inline)) {
+        const char* b = ring + (ks & 1) * 2 * TILE + a_panel + i * 32 * ROWB;
+        fa[i] = Op::read(b + fo[kc][0], b + fo[kc][1]);
+    };
+    auto read_w = [&](int ks, int kc, int j) __attribute__((always_inline)) {
+        const char* b = ring + (ks & 1) * 2 * TILE + w_panel + j * 32 * ROWB;
+        fw[kc][j] = Op::read(b + fo[kc][0], b + fo[kc][1]);
+    };
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // a region's issue order: its two MFMAs, each followed by memory
+    // instructions (LDS reads, then LDS writes, then global loads), the rest
+    // after the second
+    auto order = [&](int nrd, int nwr, int nld) __attribute__((always_inline)) {
+        const int n = nrd + nwr + nld, first = n < 2 ? n : (n + 1) / 2;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int o = 0; o < n; ++o) {
+            if (o == first) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (o < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else if (o < nrd + nwr) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        if (first >= n) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: step 0 written to stage 0, step 1 in registers, the
+    //      fragments of step 0's chunk 0 except A block 3
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) write_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) load_piece(j, nk > 1 ? 1 : 0);
+    wait_cnt<63, 0>();
+    barrier();
+#pragma unroll
+    for (int i = 0; i < 3; ++i) read_a(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) read_w(0, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int ks = 0; ks < nk; ++ks) {
+        const int kn = ks + 2 < nk ? ks + 2 : nk - 1;    // loads past the last step repeat it
+        // ---- chunk 0: A reads (block 3 of this chunk, then blocks 0-2 of
+        //      chunk 1), chunk 1's W reads in regions 0-1, piece writes, loads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i == 0) read_a(ks, 0, 3);
+            else read_a(ks, 1, i - 1);
+            if (i < 2) read_w(ks, 1, i);
+            write_piece(i, ks + 1);
+            if (i >= 2) {
+                load_piece(2 * (i - 2), kn);
+                load_piece(2 * (i - 2) + 1, kn);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) Op::mma(acc[i][j], fa[i], fw[0][j]);
+            order(i < 2 ? 4 : 2, 1, i < 2 ? 0 : 2);
+        }
+        // ---- chunk 1: block 3's A read and the piece writes in regions
+        //      0-1, the step barrier, then the next step's chunk-0 reads and
+        //      the loads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < 2) {
+                if (i == 0) read_a(ks, 1, 3);
+                write_piece(PPC + 2 * i, ks + 1);
+                write_piece(PPC + 2 * i + 1, ks + 1);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) Op::mma(acc[i][j], fa[i], fw[1][j]);
+                order(i == 0 ? 2 : 0, 2, 0);
+                if (i == 1) {
+                    // this wavefront's reads of step ks and writes of step
+                    // ks+1 are done; the barrier makes it so for all of them
+                    // (after the last step the reads below fetch a stage
+                    // nobody uses: the code stays branch-free)
+                    wait_cnt<63, 0>();
+                    barrier();
+                }
+            } else {
+                if (i == 2) {
+                    read_a(ks + 1, 0, 0);
+                    read_a(ks + 1, 0, 1);
+                    read_w(ks + 1, 0, 0);
+                    read_w(ks + 1, 0, 1);
+                } else {
+                    read_a(ks + 1, 0, 2);
+                }
+                load_piece(PPC + 2 * (i - 2), kn);
+                load_piece(PPC + 2 * (i - 2) + 1, kn);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) Op::mma(acc[i][j], fa[i], fw[1][j]);
+                order(i == 2 ? 8 : 2, 0, 2);
+            }
+        }
+    }
+}
+
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
 // the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
 // quantisation scales) before the epilogue.  STAGED selects the
@@ -654,7 +822,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
     // wavefront's panel: for the 32x32 MFMA rows 8 (r / 4) + r % 4 + 4 (l / 32)
     // of column l % 32; for 16x16x32 sub-block r / 4 holds rows
     // 16 (r / 8) + r % 4 + 4 (l / 16 % 4) of column 16 (r / 4 % 2) + l % 16.
-    constexpr bool M16 = STAGED && H3_GEMM_MFMA16;
+    constexpr bool M16 = STAGED && std::is_same<TI, bf16>::value && H3_GEMM_MFMA16;
     const int lrow = M16 ? 4 * ((lane >> 4) & 3) : 4 * (lane >> 5);
     const int lcol = M16 ? lane & 15 : lane & 31;
 
@@ -663,7 +831,10 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x16){};
-    if constexpr (STAGED) {
+    if constexpr (STAGED && std::is_same<TI, fp8>::value) {
+        static_assert(ROWB == 128 && STAGES == 2 && NWAVES == 8, "staged fp8 shape");
+        gemm_mainloop_staged_fp8(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+    } else if constexpr (STAGED) {
         static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2, "staged shape");
         if constexpr (M16) gemm_mainloop_staged16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
         else gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
@@ -1057,6 +1228,10 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
         gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
             (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
             H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+    } else if constexpr (std::is_same<TI, fp8>::value && H3_GEMM_FP8_STAGED) {
+        gemm_kernel<TI, TO, 128, 2, 8, true, EPI><<<grid, 8 * 64, 0, st>>>(
+            (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
+            H3_GEMM_GROUP_M, epi, sa, sw);
     } else {
         gemm_kernel<TI, TO, H3_GEMM_ROWB, H3_GEMM_STAGES, H3_GEMM_WAVES, false, EPI><<<grid, H3_GEMM_WAVES * 64, 0, st>>>(
             (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, H3_GEMM_GROUP_M,
