@@ -14,10 +14,12 @@
 // registers per 32-byte k-chunk: the reads of the next chunk are issued
 // before the current chunk's MFMAs.  Two ways of filling the ring:
 //   * bf16 (gemm_mainloop_staged16 on 16x16x32 MFMAs, the default, or
-//     gemm_mainloop_staged on 32x32x16): global -> registers -> LDS, spread
-//     over the step, each load landing a step before its LDS write;
-//   * fp32 and fp8 (the ring loop in gemm_kernel): buffer -> LDS DMA, one
-//     step's copies issued at the step's barrier.
+//     gemm_mainloop_staged on 32x32x16) and fp8 (gemm_mainloop_staged_fp8
+//     on 32x32x64): global -> registers -> LDS, spread over the step, each
+//     load landing a step before its LDS write;
+//   * fp32 (and fp8 when H3_GEMM_FP8_STAGED is 0; the ring loop in
+//     gemm_kernel): buffer -> LDS DMA, one step's copies issued at the
+//     step's barrier.
 // The buffer resources stop at row M (N), so tiles that run past the end are
 // padded with zeros.
 //
@@ -39,8 +41,9 @@ namespace h3 {
 // step, two LDS stages, eight wavefronts of 128 x 64, one memory instruction
 // issued beside each MFMA) on 16x16x32 MFMAs, XCD groups 4 tiles high
 // (measured best on the block's four projection shapes; four wavefronts of
-// 128 x 128, one per SIMD, ran about 4 % slower).  fp32 and fp8: the LDS-DMA ring with the H3_GEMM_* configuration,
-// groups 2 high.  The macros only exist so that other configurations of the
+// 128 x 128, one per SIMD, ran about 4 % slower).  fp8: the register-staged
+// ring on 32x32x64 MFMAs, groups 2 high.  fp32: the LDS-DMA ring with the
+// H3_GEMM_* configuration, groups 2 high.  The macros only exist so that other configurations of the
 // same templates can be built and timed.
 #ifndef H3_GEMM_ROWB
 #define H3_GEMM_ROWB 128
@@ -767,8 +770,8 @@ __device__ __forceinline__ void gemm_mainloop_staged_fp8(f32x16 (&acc)[4][2], ch
 // TI: operand type (bf16, float, fp8); T: output type.  With fp8 operands
 // the accumulators are scaled by sa[row] * sw[col] (per-row and per-column
 // quantisation scales) before the epilogue.  STAGED selects the
-// register-staged ring (bf16); otherwise the LDS-DMA ring loop below runs
-// (fp32 and fp8 operands).
+// register-staged ring (bf16 and fp8); otherwise the LDS-DMA ring loop
+// below runs (fp32 operands, or fp8 with H3_GEMM_FP8_STAGED 0).
 // row and column of accumulator element r inside its 32x32 block, less the
 // lane's own offsets (lrow, lcol in gemm_kernel)
 template <bool M16>
