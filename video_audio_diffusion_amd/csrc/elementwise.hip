@@ -58,132 +58,118 @@ __global__ __launch_bounds__(256) void adaln_kernel(const T* __restrict__ x, T* 
 }
 
 // --------------------------------------------------------------------------
-// Modulated RMSNorm over runs of rows (the wide-row form).  A workgroup of
-// 256 threads owns `rpb` consecutive rows and walks them RB at a time.
-// Thread t owns the 16-byte column vectors t, t + 256, ... of every row, so
-// its shift and scale stay in registers while the rows' modality set stays
-// the same (they are reloaded, uniformly across the workgroup, only when an
-// interval boundary changes it): the row-per-wavefront form read the 43 KB of
-// fp32 shift and scale of a 5376-wide row once per row, four times the row's
-// own bytes.  Two batches of RB rows are held in registers as stored: the
-// next batch's loads are issued before the current one is reduced per
-// wavefront, its four wavefront sums exchanged through LDS (double-buffered,
-// one barrier per batch that waits for LDS only, so loads and stores stay in
+// Modulated RMSNorm for wide rows.  A grid of at most kAdalnBlocks
+// workgroups of 256 threads sweeps the rows in step: workgroup w takes rows
+// w, w + G, w + 2G, ... (G = the grid size), so at any moment the grid
+// streams one contiguous window of about G rows, the access order that gets
+// the most out of HBM here (a grid-stride copy beats one in which each
+// workgroup streams its own contiguous run by about 8 %).  Thread t owns the
+// 16-byte column vectors t, t + 256, ... of every row, so its shift and
+// scale stay in registers while the rows' modality set stays the same (a
+// workgroup's rows only move forward, so it reloads them, uniformly, once per
+// interval boundary it crosses): the row-per-wavefront form read the 43 KB
+// of fp32 shift and scale of a 5376-wide row once per row, four times the
+// row's own bytes.  Two rows are held in registers as stored: the next
+// row's loads are issued before the current one is reduced per wavefront,
+// its four wavefront sums exchanged through LDS (double-buffered, one
+// barrier per row that waits for LDS only, so loads and stores stay in
 // flight), normalised, modulated and stored.
-// Batch of rows and grid size, measured best at 92840 x 5376 bf16 (0.41 ms,
-// against 0.43 ms for four-row batches without the second buffer and
-// 0.39 ms for a plain device copy of the same bytes).
-constexpr int kAdalnRB = 2;
-constexpr int kAdalnBlocks = 768;
+// Measured at 92840 x 5376 bf16 on a cold input: 0.370-0.373 ms at 1024
+// workgroups (5.35-5.40 TB/s), 0.376-0.44 ms at other grid sizes from 768
+// to 3072, 0.41 ms for 768 contiguous runs of rows; a grid-stride device
+// copy of the same bytes takes 0.38-0.39 ms.  Inside the block, where part
+// of x is still in the caches from the kernel before, it takes 0.354-0.356
+// ms.  Loads and stores marked non-temporal were 3 % faster on a cold input
+// but 2 % slower inside the block, so they are not used.
+constexpr int kAdalnBlocks = 1024;
 template <typename T, int VPT>
 __global__ __launch_bounds__(256) void adaln_rows_kernel(const T* __restrict__ x, T* __restrict__ y, int32_t n,
                                                          int32_t dim, const float* __restrict__ mod, int32_t br,
-                                                         SegTable tab, float eps, int32_t rpb) {
+                                                         SegTable tab, float eps) {
     constexpr int N = Vec<T>::N;
-    constexpr int RB = kAdalnRB;
-    __shared__ float part[2][RB][4];
+    __shared__ float part[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nv = dim / N;
-    const int r_begin = blockIdx.x * rpb;
-    const int r_end = min(n, r_begin + rpb);
     int cur_set = -1;
     float sh[VPT][N], sc[VPT][N];
-    // the batch at r0 as stored (zeros past the run or the row)
-    auto load_batch = [&](u32x4 (&raw)[RB][VPT], int r0) __attribute__((always_inline)) {
+    // row `row` as stored (zeros past the last row or the row's end)
+    auto load_row = [&](u32x4 (&raw)[VPT], int row) __attribute__((always_inline)) {
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const int row = r0 + b;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int j = tid + 256 * k;
-                raw[b][k] = (row < r_end && j < nv)
-                                ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(x + (int64_t)row * dim) +
-                                                                  16 * j)
-                                : (u32x4){};
-            }
+        for (int k = 0; k < VPT; ++k) {
+            const int j = tid + 256 * k;
+            raw[k] = (row < n && j < nv)
+                         ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(x + (int64_t)row * dim) + 16 * j)
+                         : (u32x4){};
         }
     };
-    auto process = [&](u32x4 (&raw)[RB][VPT], int r0, int buf) __attribute__((always_inline)) {
-        float ss[RB];
+    auto process = [&](u32x4 (&raw)[VPT], int row, int buf) __attribute__((always_inline)) {
+        float ss = 0.f;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            ss[b] = 0.f;
+        for (int k = 0; k < VPT; ++k) {
+            float f[N];
+            Vec<T>::load(&raw[k], f);
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                float f[N];
-                Vec<T>::load(&raw[b][k], f);
-#pragma unroll
-                for (int e = 0; e < N; ++e) ss[b] += f[e] * f[e];
-            }
-            ss[b] = sum_lanes<kWave>(ss[b]);
+            for (int e = 0; e < N; ++e) ss += f[e] * f[e];
         }
+        ss = sum_lanes<kWave>(ss);
         // keep the vectors packed until the second use (otherwise the
         // compiler keeps both unpacked halves live across the barrier)
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(raw[b][k]));
-        if (lane == 0) {
-#pragma unroll
-            for (int b = 0; b < RB; ++b) part[buf][b][wave] = ss[b];
-        }
+        for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(raw[k]));
+        if (lane == 0) part[buf][wave] = ss;
         // LDS-only barrier: the partial sums are visible, while this
-        // thread's loads of the next batch and stores of earlier ones stay
+        // thread's loads of the next row and stores of earlier ones stay
         // in flight
         wait_cnt<63, 0>();
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const int row = r0 + b;
-            if (row >= r_end) break;
-            const float tot = part[buf][b][0] + part[buf][b][1] + part[buf][b][2] + part[buf][b][3];
-            const float rstd = 1.0f / __builtin_sqrtf(tot / (float)dim + eps);
-            const int set = tab.s[find_seg(tab, row)].mod_set;
-            if (set != cur_set) {           // uniform: the row and the table are the workgroup's
-                cur_set = set;
-                const float* shift = mod + ((int64_t)set * 6 + 3 * br) * dim;
-#pragma unroll
-                for (int k = 0; k < VPT; ++k) {
-                    const int j = tid + 256 * k;
-                    if (j < nv) {
-#pragma unroll
-                        for (int e = 0; e < N; e += 4) {
-                            const f32x4 a = *reinterpret_cast<const f32x4*>(shift + j * N + e);
-                            const f32x4 c = *reinterpret_cast<const f32x4*>(shift + dim + j * N + e);
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                sh[k][e + u] = a[u];
-                                sc[k][e + u] = 1.0f + c[u];
-                            }
-                        }
-                    }
-                }
-            }
+        const float tot = part[buf][0] + part[buf][1] + part[buf][2] + part[buf][3];
+        const float rstd = 1.0f / __builtin_sqrtf(tot / (float)dim + eps);
+        const int set = tab.s[find_seg(tab, row)].mod_set;
+        if (set != cur_set) {           // uniform: the row and the table are the workgroup's
+            cur_set = set;
+            const float* shift = mod + ((int64_t)set * 6 + 3 * br) * dim;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int j = tid + 256 * k;
                 if (j < nv) {
-                    float f[N], o[N];
-                    Vec<T>::load(&raw[b][k], f);
 #pragma unroll
-                    for (int e = 0; e < N; ++e) o[e] = f[e] * rstd * sc[k][e] + sh[k][e];
-                    Vec<T>::store(reinterpret_cast<char*>(y + (int64_t)row * dim) + 16 * j, o);
+                    for (int e = 0; e < N; e += 4) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(shift + j * N + e);
+                        const f32x4 c = *reinterpret_cast<const f32x4*>(shift + dim + j * N + e);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            sh[k][e + u] = a[u];
+                            sc[k][e + u] = 1.0f + c[u];
+                        }
+                    }
                 }
             }
         }
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int j = tid + 256 * k;
+            if (j < nv) {
+                float f[N], o[N];
+                Vec<T>::load(&raw[k], f);
+#pragma unroll
+                for (int e = 0; e < N; ++e) o[e] = f[e] * rstd * sc[k][e] + sh[k][e];
+                Vec<T>::store(reinterpret_cast<char*>(y + (int64_t)row * dim) + 16 * j, o);
+            }
+        }
     };
-    // two batches in registers: the next batch's loads go out before this
-    // batch is reduced, normalised and stored
-    u32x4 ra[RB][VPT], rb[RB][VPT];
-    load_batch(ra, r_begin);
-    for (int r0 = r_begin; r0 < r_end; r0 += 2 * RB) {
-        load_batch(rb, r0 + RB);
-        process(ra, r0, 0);
-        if (r0 + RB >= r_end) break;
-        load_batch(ra, r0 + 2 * RB);
-        process(rb, r0 + RB, 1);
+    // two rows in registers: the next row's loads go out before this row is
+    // reduced, normalised and stored
+    u32x4 ra[VPT], rb[VPT];
+    const int G = gridDim.x;
+    load_row(ra, blockIdx.x);
+    for (int row = blockIdx.x; row < n; row += 2 * G) {
+        load_row(rb, row + G);
+        process(ra, row, 0);
+        if (row + G >= n) break;
+        load_row(ra, row + 2 * G);
+        process(rb, row + G, 1);
     }
 }
 
@@ -462,18 +448,13 @@ static hipError_t adaln_t(const void* x, void* y, int32_t n, int32_t dim, const 
 template <typename T, int VPT>
 static hipError_t adaln_rows_t(const void* x, void* y, int32_t n, int32_t dim, const float* mod, int32_t br,
                                const SegTable& tab, float eps, hipStream_t st) {
-    // kAdalnBlocks workgroups in all, each over a run of whole batches
-    const int64_t target = kAdalnBlocks;
-    int32_t rpb = (int32_t)((n + target - 1) / target);
-    rpb = (rpb + kAdalnRB - 1) / kAdalnRB * kAdalnRB;
-    if (rpb < kAdalnRB) rpb = kAdalnRB;
-    const int blocks = (n + rpb - 1) / rpb;
-    adaln_rows_kernel<T, VPT><<<blocks, 256, 0, st>>>((const T*)x, (T*)y, n, dim, mod, br, tab, eps, rpb);
+    const int blocks = n < kAdalnBlocks ? n : kAdalnBlocks;
+    adaln_rows_kernel<T, VPT><<<blocks, 256, 0, st>>>((const T*)x, (T*)y, n, dim, mod, br, tab, eps);
     return hipGetLastError();
 }
 
 // Rows of at most 4 * 64 vectors (2048 bf16 / 1024 fp32 values) keep the
-// row-per-wavefront form; wider rows take the run-of-rows form.
+// row-per-wavefront form; wider rows take the grid-sweep form.
 template <typename T>
 static hipError_t adaln_dispatch(const void* x, void* y, int32_t n, int32_t dim, const float* mod,
                                  int32_t br, const SegTable& tab, float eps, hipStream_t st) {
