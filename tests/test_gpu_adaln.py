@@ -26,7 +26,10 @@ def _segments(n, n_sets, cuts):
 
 @pytest.mark.parametrize("dtype,dim", [("bf16", 5376), ("bf16", 2560), ("bf16", 256), ("f32", 1536), ("f32", 192)])
 @pytest.mark.parametrize("n,cuts,br", [(1, (), 0), (3, (1, 2), 1), (37, (5, 6, 17, 33), 0),
-                                       (1001, (3, 250, 251, 600, 997), 1)])
+                                       (1001, (3, 250, 251, 600, 997), 1),
+                                       # more rows than the wide-row grid: each workgroup
+                                       # takes rows w, w + G, ... across interval changes
+                                       (3001, (2, 700, 701, 1023, 1025, 2047, 2999), 0)])
 def test_adaln_all_rows(dtype, dim, n, cuts, br):
     import torch
     n_sets = 3
