@@ -1,10 +1,15 @@
 """The FP8 quantisers take the quotient x / scale as the fp64 product
-x * RN64(1 / scale) rounded to fp32.  For fp32 operands this is the correctly
-rounded fp32 quotient (x / s is never an fp32 rounding midpoint and lies at
-least 2^-49 from every one, while the fp64 product is within 2^-52 of it), so
-the codes equal those of an fp32 division.  Checked here against numpy's fp32
-division on random and adversarial operand pairs (CPU only)."""
+x * RN64(1 / scale) rounded to fp32.  Where the quotient lies in fp32's
+normal range this is the correctly rounded fp32 quotient (x / s is never an
+fp32 rounding midpoint and lies at least 2^-49 from every one, while the fp64
+product is within 2^-52 of it), so the codes equal those of an fp32 division.
+Below 2^-126 the subnormal grid is fixed and the two can differ by one step;
+e4m3's smallest step is 2^-9, so both still encode to a signed zero.
+Checked here against numpy's fp32 division on random and adversarial operand
+pairs (CPU only)."""
 import numpy as np
+
+TINY = np.float32(2.0**-126)
 
 
 def _fast(x, s):
@@ -12,6 +17,8 @@ def _fast(x, s):
 
 
 def _check(x, s):
+    """Equal where the quotient is fp32-normal (or overflows); below that,
+    both below 2^-126 in magnitude with the same sign."""
     x = x.astype(np.float32)
     s = s.astype(np.float32)
     ok = np.isfinite(x) & np.isfinite(s) & (s != 0)
@@ -19,8 +26,12 @@ def _check(x, s):
     with np.errstate(over="ignore", under="ignore"):
         ref = x / s
         got = _fast(x, s)
+    normal = ~(np.abs(ref) < TINY)
     same = (ref == got) | (np.isnan(ref) & np.isnan(got))
-    assert same.all(), f"{x[~same][:4]} / {s[~same][:4]}: {ref[~same][:4]} != {got[~same][:4]}"
+    bad = normal & ~same
+    assert not bad.any(), f"{x[bad][:4]} / {s[bad][:4]}: {ref[bad][:4]} != {got[bad][:4]}"
+    sub = ~normal
+    assert (np.abs(got[sub]) < TINY).all() and (np.signbit(got[sub]) == np.signbit(ref[sub])).all()
     return x.size
 
 
@@ -52,3 +63,26 @@ def test_quotient_adversarial_significands():
     _check(x, near1)
     small = rng.integers(1, 1000, n).astype(np.float32)
     _check(small, rng.integers(1, 1000, n).astype(np.float32))
+
+
+def test_quotient_subnormal_midpoints():
+    """Quotients that are exact subnormal midpoints k * 2^-150 (k odd): the
+    fast form may round them the other way, so the identity is stated for the
+    normal range only; both results stay below 2^-126, under half of e4m3's
+    smallest subnormal 2^-9, where every value encodes to a signed zero."""
+    ms = np.arange(3, 1024, 2)
+    k = np.arange(1, 512, 2)
+    m, kk = np.meshgrid(ms, k)
+    s = (m * 2.0**20).astype(np.float32).ravel()
+    xv = (m * kk).astype(np.float64).ravel() * 2.0**-130
+    x = xv.astype(np.float32)
+    keep = x.astype(np.float64) == xv                 # representable operands only
+    x, s = x[keep], s[keep]
+    with np.errstate(under="ignore"):
+        ref = x / s
+        got = _fast(x, s)
+    assert (ref != got).any()                         # the identity does fail here
+    _check(x, s)
+    _check(-x, s)
+    assert float(np.abs(np.concatenate([ref, got])).max()) < 2.0**-10
+

@@ -27,12 +27,16 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 
 // The same codes, fast, for x / s with s finite and > 0, |x| <= the max |x|
 // the scale was taken from (so |x / s| <= 448 (1 + 2^-23)) and x not NaN:
-//  * the quotient: for fp32 x and s, x / s is never an fp32 rounding midpoint
-//    and lies at least 2^-49 (relative) from every one (x / s = midpoint
-//    would need a 25-bit odd significand from 24-bit operands; the distance
-//    is a nonzero integer over a 48-bit denominator), so rounding the fp64
-//    product x * RN64(1 / s), within 2^-52 of x / s, to fp32 gives exactly
-//    the correctly rounded fp32 quotient;
+//  * the quotient: for fp32 x and s with |x / s| in fp32's normal range,
+//    x / s is never an fp32 rounding midpoint and lies at least 2^-49
+//    (relative) from every one (x / s = midpoint would need a 25-bit odd
+//    significand from 24-bit operands; the distance is a nonzero integer
+//    over a 48-bit denominator), so rounding the fp64 product
+//    x * RN64(1 / s), within 2^-52 of x / s, to fp32 gives exactly the
+//    correctly rounded fp32 quotient.  Below 2^-126 the fp32 grid is fixed
+//    and the argument fails (the two can differ by one subnormal step), but
+//    every such quotient is far below e4m3's smallest step 2^-9 and both
+//    encode to a signed zero;
 //  * the encoding: the hardware fp32 -> e4m3 conversion gives e4m3_code's
 //    result for every fp32 value of magnitude below 464 (checked on all 2^32
 //    bit patterns; above that it returns NaN where e4m3_code saturates).
