@@ -865,21 +865,35 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_m16_kernel(
         return mx * sl2;
     };
     // exponentials of key tile kt of the logits sv under the current
-    // references, into pfr[t] words 2kt, 2kt+1; rs[t] = their sum
+    // references, into pfr[t] words 2kt, 2kt+1; rs[t] = their sum.  Written
+    // stage by stage (all eight fmas, then the exponentials, the packs, the
+    // sums) so that the VALU groups placed beside each MFMA pair hold
+    // independent instructions: half the hazard nops of the per-pair order,
+    // same values.
     auto softmax_half = [&](const f32x4 (&sv)[2][2], int kt, u32x4 (&pfr)[2], float (&rs)[2])
                             __attribute__((always_inline)) {
         const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+        float x[2][4];
+        uint32_t w[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[t][i] = __builtin_fmaf(sv[kt][t][i], sl2, -m_ref[t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[t][i] = fast_exp2(x[t][i]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                w[t][i] = pack_bf16x2(x[t][2 * i], x[t][2 * i + 1]);
+                pfr[t][2 * kt + i] = w[t][i];
+            }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            rs[t] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const float p0 = fast_exp2(__builtin_fmaf(sv[kt][t][i], sl2, -m_ref[t]));
-                const float p1 = fast_exp2(__builtin_fmaf(sv[kt][t][i + 1], sl2, -m_ref[t]));
-                const uint32_t w = pack_bf16x2(p0, p1);
-                pfr[t][2 * kt + (i >> 1)] = w;
-                rs[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, rs[t], false);
-            }
+            rs[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[t][0]), one2, 0.f, false);
+            rs[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[t][1]), one2, rs[t], false);
         }
     };
     // exponentials of a block under the current references, packed as bf16
