@@ -12,8 +12,11 @@
 // blocks of 32x32, or 8 x 4 of 16x16).  Each k-step's A and W tiles (ROWB bytes of K per row) are
 // staged in a ring of LDS stages; fragments are double-buffered in
 // registers per 32-byte k-chunk: the reads of the next chunk are issued
-// before the current chunk's MFMAs.  Two ways of filling the ring:
-//   * bf16 (gemm_mainloop_staged16 on 16x16x32 MFMAs, the default, or
+// before the current chunk's MFMAs.  Ways of filling the ring:
+//   * bf16 with K up to 8192 (gemm_mainloop_dma16 on 16x16x32 MFMAs):
+//     buffer -> LDS DMA, the copies of step s+2 spread over the regions
+//     after step s's barrier;
+//   * bf16 with larger K (gemm_mainloop_staged16 on 16x16x32 MFMAs, or
 //     gemm_mainloop_staged on 32x32x16) and fp8 (gemm_mainloop_staged_fp8
 //     on 32x32x64): global -> registers -> LDS, spread over the step, each
 //     load landing a step before its LDS write;
@@ -37,11 +40,14 @@
 
 namespace h3 {
 
-// Launch configuration.  bf16: the register-staged ring (128 bytes of K per
-// step, two LDS stages, eight wavefronts of 128 x 64, one memory instruction
-// issued beside each MFMA) on 16x16x32 MFMAs, XCD groups 4 tiles high
-// (measured best on the block's four projection shapes; four wavefronts of
-// 128 x 128, one per SIMD, ran about 4 % slower).  fp8: the register-staged
+// Launch configuration.  bf16: 128 bytes of K per step, two LDS stages,
+// eight wavefronts of 128 x 64 on 16x16x32 MFMAs, one memory instruction
+// issued beside each MFMA, XCD groups 4 tiles high (measured best on the
+// block's four projection shapes; four wavefronts of 128 x 128, one per
+// SIMD, ran about 4 % slower).  The ring is filled by LDS DMA up to
+// K = H3_GEMM_BF16_DMA_MAX_K and through registers beyond: at the block's
+// shapes the DMA loop was 2.8-4.3 % faster at K 5376 and 7168, and the
+// register-staged one 0-2.6 % faster at K 14336.  fp8: the register-staged
 // ring on 32x32x64 MFMAs, groups 2 high.  fp32: the LDS-DMA ring with the
 // H3_GEMM_* configuration, groups 2 high.  The macros only exist so that other configurations of the
 // same templates can be built and timed.
@@ -71,6 +77,9 @@ namespace h3 {
 #endif
 #ifndef H3_GEMM_MFMA16
 #define H3_GEMM_MFMA16 1
+#endif
+#ifndef H3_GEMM_BF16_DMA_MAX_K
+#define H3_GEMM_BF16_DMA_MAX_K 8192
 #endif
 #ifndef H3_GEMM_FP8_STAGED
 #define H3_GEMM_FP8_STAGED 1
@@ -175,6 +184,12 @@ __device__ __forceinline__ void copy_operand(char* lds, int wave, const void* ba
     for (int j = 0; j < PIECES; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(lds + (wave * PIECES + j) * 1024), 16, voff[j], koff, 0,
                                                  0);
+}
+
+// One 1 KB piece by buffer -> LDS DMA: lane l's 16 bytes at voff + soff of
+// the buffer land at dst + 16 l.
+__device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, H3_LDS(dst), 16, voff, soff, 0, 0);
 }
 
 // Epilogues.  EpiStore writes C.  EpiGate writes out = x + gate * C with
@@ -602,6 +617,154 @@ __device__ __forceinline__ void gemm_mainloop_staged16(f32x16 (&acc)[4][NWAVES =
             for (int e = 0; e < 4; ++e) acc[ib >> 1][jb >> 1][4 * (2 * (ib & 1) + (jb & 1)) + e] = c16[ib][jb][e];
 }
 
+// ---------------------------------------------------------------- LDS-DMA ring on 16x16x32 MFMAs (bf16)
+// gemm_mainloop_staged16's fragment schedule with the tile pieces copied by
+// buffer -> LDS DMA instead of through registers: the same 1 KB pieces land
+// at the same LDS addresses, so the fragments and sums are the same.  The
+// copies of step ks+2 go out in regions 2-7 of chunk 1 of step ks, right
+// after the step barrier that frees stage ks % 2, and have until the
+// barrier of step ks+1 to land: that barrier waits for every copy the
+// wavefront has in flight (vmcnt 0), which are exactly those.
+template <int NWAVES>
+__device__ __forceinline__ void gemm_mainloop_dma16(f32x16 (&acc)[4][NWAVES == 4 ? 4 : 2], char* ring,
+                                                    const bf16* __restrict__ A, int64_t lda,
+                                                    const bf16* __restrict__ W, int64_t ldw, int32_t M, int32_t N,
+                                                    int32_t K, int m0, int n0, int wave, int lane) {
+    constexpr int ROWB = 128, KCH = 2;
+    using Geo = GemmGeom<ROWB, 2, NWAVES, 64>;
+    constexpr int NJ = Geo::NJ;
+    constexpr int NB = 2 * NJ;
+    constexpr int TILE = Geo::TILE;
+    constexpr int PIECES = Geo::PIECES;
+    constexpr int NP = 2 * PIECES;
+    static_assert(NWAVES == 8 && PIECES == 4 && NB == 4, "DMA ring layout");
+    const int wm = wave >> 2, wn = wave & 3;
+
+    const uint32_t ldab = (uint32_t)(lda * 2), ldwb = (uint32_t)(ldw * 2);
+    uint32_t voff[NP];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+        const int row = Geo::ROWS_PER_WAVE * wave + Geo::ROWS_PER_PIECE * j + lane / Geo::CPR;
+        const uint32_t c = (uint32_t)Geo::slot(row, lane % Geo::CPR);
+        voff[j] = (uint32_t)row * ldab + c * 16;
+        voff[PIECES + j] = (uint32_t)row * ldwb + c * 16;
+    }
+    const uint32_t bytes_a = (uint32_t)(M - m0 < kBM ? M - m0 : kBM) * ldab;
+    const uint32_t bytes_w = (uint32_t)(N - n0 < kBN ? N - n0 : kBN) * ldwb;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (int64_t)m0 * lda, bytes_a);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * ldw, bytes_w);
+    const int nk = K / 64;
+    auto copy_piece = [&](int j, int ks) __attribute__((always_inline)) {
+        char* st = ring + (ks & 1) * 2 * TILE + (j < PIECES ? 0 : TILE) + (wave * PIECES + j % PIECES) * 1024;
+        dma_piece(j < PIECES ? ra : rw, st, voff[j], (uint32_t)ks * ROWB);
+    };
+
+    const int frow = lane & 15, fq = lane >> 4;
+    uint32_t fo[KCH];
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) fo[kc] = (uint32_t)(frow * ROWB + (Geo::slot(frow, 4 * kc + fq) << 4));
+    const int a_panel = wm * 128 * ROWB, w_panel = TILE + wn * NJ * 32 * ROWB;
+    u32x4 fa[8], fw[2][NB];
+    auto read_a = [&](int ks, int kc, int ib) __attribute__((always_inline)) {
+        fa[ib] = *reinterpret_cast<const u32x4*>(ring + (ks & 1) * 2 * TILE + a_panel + ib * 16 * ROWB + fo[kc]);
+    };
+    auto read_w = [&](int ks, int kc, int jb) __attribute__((always_inline)) {
+        fw[kc][jb] = *reinterpret_cast<const u32x4*>(ring + (ks & 1) * 2 * TILE + w_panel + jb * 16 * ROWB + fo[kc]);
+    };
+    f32x4 c16[8][NB];
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) c16[ib][jb] = (f32x4){};
+    auto mfma = [&](int kc, int ib, int jb) __attribute__((always_inline)) {
+        c16[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[ib]),
+                                                              __builtin_bit_cast(bf16x8, fw[kc][jb]), c16[ib][jb],
+                                                              0, 0, 0);
+    };
+    auto barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto order = [&](int nrd, int nld) __attribute__((always_inline)) {
+        int m = 0;
+#pragma unroll
+        for (int o = 0; o < nrd + nld; ++o) {
+            if (m < NB) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                ++m;
+            }
+            if (o < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (; m < NB; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: steps 0 and 1 copied, step 0 landed and visible; the
+    //      fragments of step 0's chunk 0 except A block 7
+#pragma unroll
+    for (int j = 0; j < NP; ++j) copy_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) copy_piece(j, nk > 1 ? 1 : 0);
+    wait_cnt<NP, 0>();
+    barrier();
+#pragma unroll
+    for (int ib = 0; ib < 7; ++ib) read_a(0, 0, ib);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) read_w(0, 0, jb);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int ks = 0; ks < nk; ++ks) {
+        const int kn = ks + 2 < nk ? ks + 2 : nk - 1;    // copies past the last step repeat it
+        // ---- chunk 0: fragment reads only
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            if (ib == 0) read_a(ks, 0, 7);
+            else read_a(ks, 1, ib - 1);
+            if (ib < 4) read_w(ks, 1, ib);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) mfma(0, ib, jb);
+            order(ib < 4 ? 2 : 1, 0);
+        }
+        // ---- chunk 1
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            if (ib < 2) {
+                if (ib == 0) read_a(ks, 1, 7);
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) mfma(1, ib, jb);
+                order(ib == 0 ? 1 : 0, 0);
+                if (ib == 1) {
+                    // this wavefront's reads of step ks are done and its copies
+                    // of step ks+1 have landed; the barrier makes it so for all
+                    wait_cnt<0, 0>();
+                    barrier();
+                }
+            } else {
+                if (ib == 2) read_a(ks + 1, 0, 0);
+                read_a(ks + 1, 0, ib - 1);
+                if (ib < 6) read_w(ks + 1, 0, ib - 2);
+                const int nc = ib < 4 ? 2 : 1;            // copies 0-1, 2-3, 4, 5, 6, 7
+                const int c0 = ib < 4 ? 2 * (ib - 2) : ib;
+#pragma unroll
+                for (int q = 0; q < nc; ++q) copy_piece(c0 + q, kn);
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) mfma(1, ib, jb);
+                order((ib == 2 ? 2 : 1) + (ib < 6 ? 1 : 0), nc);
+            }
+        }
+    }
+    wait_cnt<0, 0>();    // no copy may land after the loop (the epilogue may reuse the ring)
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[ib >> 1][jb >> 1][4 * (2 * (ib & 1) + (jb & 1)) + e] = c16[ib][jb][e];
+}
+
 // ---------------------------------------------------------------- staged ring for fp8 operands
 // The register-staged ring of gemm_mainloop_staged16 (same pieces, loads a
 // step ahead, LDS writes, barrier) for e4m3 operands on the 32x32x64 MFMA of
@@ -783,7 +946,7 @@ __device__ __forceinline__ constexpr int acc_col(int r) {
     return M16 ? 16 * ((r >> 2) & 1) : 0;
 }
 
-template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, bool STAGED, typename EPI>
+template <typename TI, typename T, int ROWB, int STAGES, int NWAVES, bool STAGED, typename EPI, bool DMA16 = false>
 __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict__ A, int64_t lda,
                                                    const TI* __restrict__ W, int64_t ldw,
                                                    T* __restrict__ C, int64_t ldc, int32_t M, int32_t N,
@@ -839,7 +1002,9 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         gemm_mainloop_staged_fp8(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
     } else if constexpr (STAGED) {
         static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2, "staged shape");
-        if constexpr (M16) gemm_mainloop_staged16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+        if constexpr (M16 && DMA16 && NWAVES == 8)
+            gemm_mainloop_dma16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
+        else if constexpr (M16) gemm_mainloop_staged16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
         else gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
     } else {
         // ---- copy offsets: piece j of this wavefront holds tile rows
@@ -1228,9 +1393,16 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
     const int grid = tiles_m * tiles_n;
     constexpr bool BF = std::is_same<TI, bf16>::value;
     if constexpr (BF && H3_GEMM_BF16_STAGED) {
-        gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
-            (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-            H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+        // the LDS-DMA loop for K up to H3_GEMM_BF16_DMA_MAX_K (measured faster at
+        // K 5376 and 7168), the register-staged loop beyond (faster at 14336)
+        if (H3_GEMM_BF16_WAVES == 8 && K <= H3_GEMM_BF16_DMA_MAX_K)
+            gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI, true><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
+                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
+                H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+        else
+            gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
+                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
+                H3_GEMM_BF16_GROUP_M, epi, sa, sw);
     } else if constexpr (std::is_same<TI, fp8>::value && H3_GEMM_FP8_STAGED) {
         gemm_kernel<TI, TO, 128, 2, 8, true, EPI><<<grid, 8 * 64, 0, st>>>(
             (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
