@@ -637,8 +637,10 @@ __device__ __forceinline__ void gemm_mainloop_dma16(f32x16 (&acc)[4][NWAVES == 4
     constexpr int TILE = Geo::TILE;
     constexpr int PIECES = Geo::PIECES;
     constexpr int NP = 2 * PIECES;
-    static_assert(NWAVES == 8 && PIECES == 4 && NB == 4, "DMA ring layout");
-    const int wm = wave >> 2, wn = wave & 3;
+    static_assert((NWAVES == 8 && PIECES == 4 && NB == 4) || (NWAVES == 4 && PIECES == 8 && NB == 8), "DMA ring layout");
+    constexpr int W4 = NB / 4;                           // W blocks read per region
+    const int wm = NWAVES == 4 ? wave >> 1 : wave >> 2;
+    const int wn = NWAVES == 4 ? wave & 1 : wave & 3;
 
     const uint32_t ldab = (uint32_t)(lda * 2), ldwb = (uint32_t)(ldw * 2);
     uint32_t voff[NP];
@@ -723,10 +725,13 @@ __device__ __forceinline__ void gemm_mainloop_dma16(f32x16 (&acc)[4][NWAVES == 4
         for (int ib = 0; ib < 8; ++ib) {
             if (ib == 0) read_a(ks, 0, 7);
             else read_a(ks, 1, ib - 1);
-            if (ib < 4) read_w(ks, 1, ib);
+            if (ib < 4) {
+#pragma unroll
+                for (int q = 0; q < W4; ++q) read_w(ks, 1, W4 * ib + q);
+            }
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) mfma(0, ib, jb);
-            order(ib < 4 ? 2 : 1, 0);
+            order(ib < 4 ? 1 + W4 : 1, 0);
         }
         // ---- chunk 1
 #pragma unroll
@@ -745,14 +750,20 @@ __device__ __forceinline__ void gemm_mainloop_dma16(f32x16 (&acc)[4][NWAVES == 4
             } else {
                 if (ib == 2) read_a(ks + 1, 0, 0);
                 read_a(ks + 1, 0, ib - 1);
-                if (ib < 6) read_w(ks + 1, 0, ib - 2);
-                const int nc = ib < 4 ? 2 : 1;            // copies 0-1, 2-3, 4, 5, 6, 7
-                const int c0 = ib < 4 ? 2 * (ib - 2) : ib;
+                if (ib < 6) {
+#pragma unroll
+                    for (int q = 0; q < W4; ++q) read_w(ks + 1, 0, W4 * (ib - 2) + q);
+                }
+                // the NP copies over regions 2-7: 8 waves 2, 2, 1, 1, 1, 1;
+                // 4 waves 3, 3, 3, 3, 2, 2
+                constexpr int HI = NP == 8 ? 2 : 3, LO = NP == 8 ? 1 : 2;
+                const int nc = ib < (NP == 8 ? 4 : 6) ? HI : LO;
+                const int c0 = NP == 8 ? (ib < 4 ? 2 * (ib - 2) : ib) : (ib < 6 ? 3 * (ib - 2) : 12 + 2 * (ib - 6));
 #pragma unroll
                 for (int q = 0; q < nc; ++q) copy_piece(c0 + q, kn);
 #pragma unroll
                 for (int jb = 0; jb < NB; ++jb) mfma(1, ib, jb);
-                order((ib == 2 ? 2 : 1) + (ib < 6 ? 1 : 0), nc);
+                order((ib == 2 ? 2 : 1) + (ib < 6 ? W4 : 0), nc);
             }
         }
     }
@@ -1002,7 +1013,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
         gemm_mainloop_staged_fp8(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
     } else if constexpr (STAGED) {
         static_assert(std::is_same<TI, bf16>::value && ROWB == 128 && STAGES == 2, "staged shape");
-        if constexpr (M16 && DMA16 && NWAVES == 8)
+        if constexpr (M16 && DMA16)
             gemm_mainloop_dma16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
         else if constexpr (M16) gemm_mainloop_staged16<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
         else gemm_mainloop_staged<NWAVES>(acc, ring, A, lda, W, ldw, M, N, K, m0, n0, wave, lane);
@@ -1395,7 +1406,7 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
     if constexpr (BF && H3_GEMM_BF16_STAGED) {
         // the LDS-DMA loop for K up to H3_GEMM_BF16_DMA_MAX_K (measured faster at
         // K 5376 and 7168), the register-staged loop beyond (faster at 14336)
-        if (H3_GEMM_BF16_WAVES == 8 && K <= H3_GEMM_BF16_DMA_MAX_K)
+        if (K <= H3_GEMM_BF16_DMA_MAX_K)
             gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI, true><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
                 (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
                 H3_GEMM_BF16_GROUP_M, epi, sa, sw);
