@@ -252,8 +252,10 @@ def test_attention_peaked_full_width():
     assert_close("attn_peaked", widen(o, "bf16")[rows], ref, TB)
 
 
+# K up to 8192 runs the LDS-DMA main loop, larger K the register-staged one:
+# both at ragged M and N, and K at the switch point
 @pytest.mark.parametrize("M,N,K", [(1, 8, 64), (255, 200, 192), (257, 264, 576), (1000, 512, 64),
-                                   (513, 1032, 1024)])
+                                   (513, 1032, 1024), (300, 200, 8192), (257, 264, 8256), (1, 8, 8256)])
 def test_gemm_ragged(M, N, K):
     import torch
     from video_audio_diffusion_amd.block import device_inputs
@@ -266,11 +268,13 @@ def test_gemm_ragged(M, N, K):
     assert_close(f"gemm {M}x{N}x{K}", widen(c, "bf16"), ref, TB)
 
 
-def test_gemm_strided_views():
-    """Row strides wider than the rows (the o -> y projection reads a view)."""
+@pytest.mark.parametrize("K", [128, 8256])
+def test_gemm_strided_views(K):
+    """Row strides wider than the rows (the o -> y projection reads a view),
+    through both main loops."""
     import torch
     from video_audio_diffusion_amd.block import device_inputs
-    M, N, K = 300, 264, 128
+    M, N = 300, 264
     a_h, w_h = _rand((M, 3 * K), 9), _rand((N, 2 * K), 10)
     d = device_inputs(None, {"a": a_h, "w": w_h})
     c = torch.zeros(M, 2 * N, dtype=torch.bfloat16, device="cuda")

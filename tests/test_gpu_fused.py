@@ -42,7 +42,8 @@ def _dev(a):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K,n_sets,br,inplace,pad", [
     (1, 8, 64, 1, 0, False, 0), (300, 264, 128, 4, 0, True, 0), (257, 520, 192, 3, 1, False, 8),
-    (513, 256, 64, 4, 1, True, 16), (1536, 512, 64, 6, 0, False, 0), (1280, 264, 128, 2, 1, True, 8)])
+    (513, 256, 64, 4, 1, True, 16), (1536, 512, 64, 6, 0, False, 0), (1280, 264, 128, 2, 1, True, 8),
+    (300, 264, 8256, 3, 1, True, 8)])    # K past the LDS-DMA loop's limit: the register-staged loop
 def test_gemm_gate_residual(dtype, M, N, K, n_sets, br, inplace, pad):
     import torch
     ldo = N + pad
@@ -73,7 +74,8 @@ def test_gemm_gate_residual(dtype, M, N, K, n_sets, br, inplace, pad):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,F,K,pad", [(1, 32, 64, 0), (257, 96, 128, 0), (300, 160, 192, 8), (513, 288, 64, 0)])
+@pytest.mark.parametrize("M,F,K,pad", [(1, 32, 64, 0), (257, 96, 128, 0), (300, 160, 192, 8), (513, 288, 64, 0),
+                                        (257, 96, 8256, 8)])
 def test_gemm_swiglu(dtype, M, F, K, pad):
     import torch
     a_h = inputs.draw_rows(None, (M, K), 41 + M, dtype=dtype)

@@ -59,6 +59,7 @@ SPLIT = {128: (64, 32, 32), 64: (16, 24, 24)}
     ("bf16", 513, 4, 64, 192, "mixed", 0, False, None),
     ("bf16", 1100, 6, 128, 64, "mixed", 0, True, None),
     ("bf16", 300, 2, 128, 64, "mixed", 0, True, 8),
+    ("bf16", 257, 2, 128, 8256, "mixed", 8, True, None),     # K past the LDS-DMA loop's limit
     ("f32", 72, 4, 64, 192, "mixed", 0, True, None),
     ("f32", 257, 2, 128, 64, "mixed", 8, False, None),
 ])
