@@ -1405,15 +1405,18 @@ hipError_t launch_gemm_t(const void* A, int64_t lda, const void* W, int64_t ldw,
     constexpr bool BF = std::is_same<TI, bf16>::value;
     if constexpr (BF && H3_GEMM_BF16_STAGED) {
         // the LDS-DMA loop for K up to H3_GEMM_BF16_DMA_MAX_K (measured faster at
-        // K 5376 and 7168), the register-staged loop beyond (faster at 14336)
+        // K 5376 and 7168), the register-staged loop beyond (faster at 14336);
+        // XCD groups 2 tiles high when the output is at most 32 tiles wide (the
+        // 5376-wide projections, 3 % faster), else H3_GEMM_BF16_GROUP_M
+        const int gm = tiles_n <= 32 ? 2 : H3_GEMM_BF16_GROUP_M;
         if (K <= H3_GEMM_BF16_DMA_MAX_K)
             gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI, true><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
-                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-                H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, gm, epi, sa,
+                sw);
         else
             gemm_kernel<TI, TO, 128, 2, H3_GEMM_BF16_WAVES, true, EPI><<<grid, H3_GEMM_BF16_WAVES * 64, 0, st>>>(
-                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
-                H3_GEMM_BF16_GROUP_M, epi, sa, sw);
+                (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n, gm, epi, sa,
+                sw);
     } else if constexpr (std::is_same<TI, fp8>::value && H3_GEMM_FP8_STAGED) {
         gemm_kernel<TI, TO, 128, 2, 8, true, EPI><<<grid, 8 * 64, 0, st>>>(
             (const TI*)A, lda, (const TI*)W, ldw, (TO*)C, ldc, (int32_t)M, N, K, tiles_m, tiles_n,
