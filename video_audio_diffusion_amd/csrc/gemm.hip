@@ -1204,7 +1204,69 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_kernel(const TI* __restrict_
                            : gbase[epi.tab.s[find_seg(epi.tab, row)].mod_set * set_stride + j * 32 + cof(r)];
         };
         const int64_t obase = (int64_t)(m0 + wm * 128 + lrow) * ldc + n0 + wn * NJ * 32 + lcol;
-        if (full) {
+        // bf16 output of a full tile (staged and DMA loops, whose 128 KB ring
+        // is free now): the fp32 products go through LDS, 128 tile rows per
+        // pass, so that x is read and out written as 16-byte vectors of eight
+        // columns of one row (a wavefront covers two 512-byte row runs)
+        // instead of the accumulators' 2-byte scatter.  Same arithmetic as
+        // below: out = bf16(x + gate * acc).
+        constexpr bool LDS_GATE = std::is_same<T, bf16>::value && STAGED && STAGES * 2 * TILE >= 128 * 1024;
+        if (LDS_GATE && full) {
+            // 16-byte chunk c (four columns) of tile row rl at slot c ^ (rl % 64)
+            auto fchunk = [&](int rl, int c) __attribute__((always_inline)) -> float* {
+                return reinterpret_cast<float*>(ring + rl * 1024 + ((c ^ (rl & 63)) << 4));
+            };
+            const int cg = tid & 31;                          // this thread's eight columns: 8 cg ..
+            const float* gcol = epi.mod + (int64_t)epi.chunk * N + n0 + 8 * cg;
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = gcol[set0 * set_stride + e];
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                __syncthreads();          // the ring is free (main loop, or the previous pass, done)
+                if (wm == pass) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int rl = i * 32 + rof(r) + lrow;
+                                const int col = wn * NJ * 32 + j * 32 + cof(r) + lcol;
+                                fchunk(rl, col >> 2)[col & 3] = acc[i][j][r];
+                            }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int rl = (tid >> 5) + 16 * k;
+                    const int row = m0 + pass * 128 + rl;
+                    const f32x4 a0 = *reinterpret_cast<const f32x4*>(fchunk(rl, 2 * cg));
+                    const f32x4 a1 = *reinterpret_cast<const f32x4*>(fchunk(rl, 2 * cg + 1));
+                    const int64_t o = (int64_t)row * ldc + n0 + 8 * cg;
+                    const u32x4 xw = *reinterpret_cast<const u32x4*>(xb + o);
+                    const float* gr = one_set ? nullptr : gcol + epi.tab.s[find_seg(epi.tab, row)].mod_set * set_stride;
+                    float xv[8], av[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // a bf16 widens to fp32 by its bits moved to the top half
+                        const uint32_t w = xw[e];
+                        xv[2 * e] = __builtin_bit_cast(float, w << 16);
+                        xv[2 * e + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+                        av[e] = a0[e];
+                        av[4 + e] = a1[e];
+                    }
+                    u32x4 ow;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float g0e = one_set ? gv[2 * e] : gr[2 * e];
+                        const float g1e = one_set ? gv[2 * e + 1] : gr[2 * e + 1];
+                        ow[e] = pack_bf16x2(xv[2 * e] + g0e * av[2 * e], xv[2 * e + 1] + g1e * av[2 * e + 1]);
+                    }
+                    *reinterpret_cast<u32x4*>(C + o) = ow;
+                }
+            }
+        } else if (full) {
             // per 32-row block: all 16 x NJ residual loads first, then the stores
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
