@@ -1,5 +1,6 @@
 // Device-side helpers shared by the libh3blk kernels (gfx950 only).
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -88,11 +89,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---------------------------------------------------------------- reductions
+// Sum over aligned groups of WIDTH lanes by the xor butterfly (masks
+// WIDTH/2, ..., 1), every lane ending with its group's total.  For WIDTH 16
+// the steps are DPP moves inside each 16-lane row instead of LDS permutes:
+// row_ror:8 is lane ^ 8; after that step the values are symmetric under
+// ^ 8, so row_ror:4 delivers lane ^ 4's value; quad_perm gives ^ 2 and ^ 1.
+// The same pairs are added in the same order, so the sums are identical.
 template <int WIDTH>
 __device__ __forceinline__ float sum_lanes(float v) {
+    if constexpr (WIDTH == 16) {
+        auto dpp = [](float x, auto ctrl) __attribute__((always_inline)) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                      decltype(ctrl)::value, 0xF, 0xF, true));
+        };
+        v += dpp(v, std::integral_constant<int, 0x128>{});   // row_ror:8
+        v += dpp(v, std::integral_constant<int, 0x124>{});   // row_ror:4
+        v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+        v += dpp(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+        return v;
+    } else {
 #pragma unroll
-    for (int m = WIDTH / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+        for (int m = WIDTH / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+        return v;
+    }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
